@@ -1,0 +1,179 @@
+"""Plain fp64 CPU oracle for paged decode attention, its KV write and its
+copy-on-write block copy.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline are the only callers.  The product path never imports this package,
+and this package imports nothing from the product path.  The arithmetic lives
+in ``oracle.c`` (plain C, gcc, OpenMP over (sequence, head) pairs); this file
+only builds it and marshals numpy arrays.
+
+What each function follows on the pages (Kwon et al., PagedAttention):
+
+* :func:`decode` -- zhaifeiyue.github.io summary, "method" paragraph, the
+  block-wise equation for ``A_ij`` and ``o_i``; block tables per wywy.jp
+  Keyword "Block table" and ricepunchb.github.io section 3.2.
+* :func:`write_kv` -- wywy.jp Keyword "autoregressive generation phase" and
+  "KV cache manager" (next free position of the last block).
+* :func:`copy_blocks` -- wywy.jp WHERE, parallel-sampling copy-on-write
+  example; zhaifeiyue memory-management table, "Copy-on-Write".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+F16 = 0
+F32 = 1
+
+_STATUS = {0: "ok", -1: "bad argument", -2: "block table entry out of range",
+           -3: "bad or repeated slot", -4: "bad copy pairs"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc (no fast-math, no intrinsics)."""
+    if not force and os.path.exists(LIBRARY):
+        return LIBRARY
+    tmp = LIBRARY + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+           "-o", tmp, SOURCE, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_to_double_array.argtypes = [vp, vp, i64]
+        lib.oracle_half_to_double_array.restype = None
+        lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      f32, i32, vp, i32, vp, i32, i32]
+        lib.oracle_decode.restype = i32
+        lib.oracle_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
+        lib.oracle_write_kv.restype = i32
+        lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
+        lib.oracle_copy_blocks.restype = i32
+        lib.oracle_threads_available.argtypes = []
+        lib.oracle_threads_available.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.float16:
+        return F16
+    if arr.dtype == np.float32:
+        return F32
+    raise OracleError(f"unsupported element type {arr.dtype}")
+
+
+def _ptr(arr):
+    return None if arr is None else arr.ctypes.data
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what}: {_STATUS.get(rc, rc)}")
+
+
+def threads_available() -> int:
+    return int(_load().oracle_threads_available())
+
+
+def half_to_double(bits: np.ndarray) -> np.ndarray:
+    """Decode uint16 binary16 bit patterns to float64 with the oracle's own decoder."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_half_to_double_array(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, scale, *,
+           pairs=None, return_weights=False, threads=0):
+    """fp64 paged decode attention.
+
+    q: [N][H][D]; pools: [NB][H][B][D] (float16 or float32, same type as q);
+    block_tables: int32 [N][MB]; context_lens: int32 [N]; scale: fp32 value.
+    pairs: optional int array [P][2] of (b, h) to compute; other rows of the
+    result stay NaN.  Returns float64 [N][H][D] (and weights [N][H][max ctx]
+    when asked, NaN past each context).
+    """
+    q = np.ascontiguousarray(q)
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    dt = _dtype_code(q)
+    if _dtype_code(k_pool) != dt or _dtype_code(v_pool) != dt:
+        raise OracleError("q, k_pool and v_pool must share one element type")
+    N, H, D = q.shape
+    NB, H2, B, D2 = k_pool.shape
+    if (H2, D2) != (H, D) or v_pool.shape != k_pool.shape:
+        raise OracleError("pool shape does not match q")
+    MB = tables.shape[1] if tables.ndim == 2 else 0
+    if tables.shape[0] != N or ctx.shape != (N,):
+        raise OracleError("block_tables / context_lens do not match the batch")
+    out = np.full((N, H, D), np.nan, dtype=np.float64)
+    pair_arr = None
+    npairs = 0
+    if pairs is not None:
+        pair_arr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        npairs = pair_arr.shape[0]
+    w = None
+    wstride = 0
+    if return_weights:
+        wstride = max(int(ctx.max()) if N else 0, 1)
+        w = np.full((N, H, wstride), np.nan, dtype=np.float64)
+    rc = _load().oracle_decode(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(tables),
+                               _ptr(ctx), N, H, D, B, NB, MB, float(np.float32(scale)), dt,
+                               _ptr(pair_arr), npairs, _ptr(w), wstride, int(threads))
+    _check(rc, "oracle decode")
+    return (out, w) if return_weights else out
+
+
+def write_kv(key, value, k_pool, v_pool, slot_mapping):
+    """Scatter key/value [T][H][D] into the pools in place (bit copies)."""
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    for p in (k_pool, v_pool):
+        if not p.flags.c_contiguous:
+            raise OracleError("pools must be C-contiguous (written in place)")
+    dt = _dtype_code(key)
+    T, H, D = key.shape
+    NB, _, B, _ = k_pool.shape
+    rc = _load().oracle_write_kv(_ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slots),
+                                 T, H, D, B, NB, dt)
+    _check(rc, "oracle write_kv")
+
+
+def copy_blocks(k_pool, v_pool, block_mapping):
+    """Copy whole physical blocks src -> dst in both pools, in place."""
+    pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    for p in (k_pool, v_pool):
+        if not p.flags.c_contiguous:
+            raise OracleError("pools must be C-contiguous (written in place)")
+    NB, H, B, D = k_pool.shape
+    rc = _load().oracle_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
+                                    H, D, B, NB, _dtype_code(k_pool))
+    _check(rc, "oracle copy_blocks")

@@ -1,0 +1,475 @@
+"""Seeded synthetic inputs shaped like the PagedAttention pages' workloads.
+
+This module draws context lengths, block placements and K/V/q values, and
+lays the values out in block pools.  It holds none of the attention
+arithmetic and imports neither the oracle nor the GPU library; both sides of
+every parity test take their inputs from here.
+
+Shapes and value recipe
+-----------------------
+* K, V and q are standard normal, drawn in fp32 and rounded to the element
+  type (round to nearest even).  K/V are drawn per sequence in logical token
+  order, so the same logical values exist for every block size and every
+  placement.
+* Pools are [num_blocks][num_heads][block_size][head_dim]; K and V live in
+  two separate pools indexed by one block table (the wywy.jp notes, Keyword
+  "PagedAttention", say the paper keeps K and V in separate blocks).
+* Physical blocks are a seeded random permutation of a pool 1.5x the size of
+  the blocks in use ("randomly scattered"); sequences take consecutive slices
+  of the permutation in logical-block order.
+* Every slot that holds no token (unused blocks, the tail of each last block)
+  is NaN, so a kernel that reads an unused slot shows it.
+* Block-table entries past a sequence's last block are -1.
+
+Each workload describes one decoding step: first the copy-on-write block
+copies (``block_mapping``), then the write of new tokens (``slot_mapping``,
+``new_key``, ``new_value``), then the decode over ``context_lens``.  With
+host fill it also carries the pools before the step (``k_pool_pre``) and
+after it (``k_pool``).
+
+The configurations
+------------------
+1. tiny fp32: 4 sequences, contexts {1, 17, 33, 50}, 2 heads, head_dim 64,
+   B = 16, 32 physical blocks, scale 1/sqrt(64); the step also forks the
+   fourth sequence (one copy-on-write copy of its last block), so the decode
+   batch holds 5 rows.
+2. OPT-13B layer: 64 sequences, 40 heads, head_dim 128, fp16, B = 16,
+   contexts lognormal (median 300, sigma 0.9) clipped to [1, 2048].
+3. short requests: 256 sequences, contexts uniform in [20, 200], B in
+   {8, 16, 32, 64} with the same sequences and logical K/V for every B.
+4. shared prefix / copy-on-write: 32 prompts (length uniform [64, 512]) with
+   6 samples each (refcount 6 on the prompt's blocks) and private tails of
+   uniform [1, 256] tokens; the partial last prompt block is copied for 5 of
+   the 6 samples, the 6th keeps the original.
+5. long context: 32 sequences, 96 heads, head_dim 128, fp16, B = 16,
+   contexts uniform in [4096, 16384].
+
+These stand in for the ShareGPT (long, high-variance) and Alpaca (short)
+request mixes the pages evaluate on; no dataset is read.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F16 = "f16"
+F32 = "f32"
+NP_DTYPES = {F16: np.float16, F32: np.float32}
+ELEM_BYTES = {F16: 2, F32: 4}
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    dtype: str
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    context_lens: np.ndarray          # int32 [N]
+    block_tables: np.ndarray          # int32 [N][MB], -1 past the live entries
+    scale: np.float32
+    q: np.ndarray                     # [N][H][D] in the element type
+    block_mapping: np.ndarray         # int64 [P][2] copy-on-write (src, dst)
+    new_key: np.ndarray               # [T][H][D] tokens written by the step
+    new_value: np.ndarray
+    slot_mapping: np.ndarray          # int64 [T]
+    logical_k: list | None = None          # host fill: per sequence [ctx][H][D]
+    logical_v: list | None = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def np_dtype(self):
+        return NP_DTYPES[self.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+    @property
+    def pool_shape(self):
+        return (self.num_blocks, self.num_heads, self.block_size, self.head_dim)
+
+    def algorithmic_bytes(self) -> int:
+        return algorithmic_bytes(self.context_lens, self.num_heads, self.head_dim,
+                                 self.block_size, self.elem_bytes)
+
+
+def algorithmic_bytes(context_lens, num_heads, head_dim, block_size, elem_bytes) -> int:
+    """Bytes a decode call must move at minimum: every context token's K and V
+    row for every head, plus one 4-byte table entry per block in use."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    blocks = (ctx + block_size - 1) // block_size
+    return int(ctx.sum() * num_heads * head_dim * 2 * elem_bytes + 4 * blocks.sum())
+
+
+def kv_bytes_per_token(num_heads, head_dim, elem_bytes, num_layers=1) -> int:
+    """K plus V bytes one token occupies across `num_layers` layers."""
+    return 2 * num_heads * head_dim * elem_bytes * num_layers
+
+
+def _blocks_for(n: int, B: int) -> int:
+    return -(-int(n) // B)
+
+
+def _normal(rng, shape, dtype):
+    return rng.standard_normal(shape, dtype=np.float32).astype(dtype)
+
+
+def _draw_kv(seed_seqs, lengths, H, D, dtype):
+    """K then V, [n][H][D] each, from one child stream per entry.  Streams
+    are independent, so drawing them on worker threads is deterministic."""
+    def one(i):
+        r = np.random.default_rng(seed_seqs[i])
+        return _normal(r, (int(lengths[i]), H, D), dtype), _normal(r, (int(lengths[i]), H, D), dtype)
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(one, range(len(lengths))))
+    return [r[0] for r in res], [r[1] for r in res]
+
+
+def _place(pool, seq_vals, phys_blocks, B):
+    """Lay a sequence's logical rows [n][H][D] into its physical blocks,
+    block-granular: logical rows are grouped B at a time (the last group
+    padded with NaN) and each group is stored as one block."""
+    n, H, D = seq_vals.shape
+    nblk = len(phys_blocks)
+    padded = np.full((nblk * B, H, D), np.nan, dtype=pool.dtype)
+    padded[:n] = seq_vals
+    pool[np.asarray(phys_blocks, dtype=np.int64)] = padded.reshape(nblk, B, H, D).transpose(0, 2, 1, 3)
+
+
+def _next_slot(table_row, tokens_stored, B):
+    """Where the manager stores the next token of a sequence that already
+    holds `tokens_stored` tokens: the next free position of its last block,
+    or position 0 of its next block when the last one is full."""
+    blocks_used = _blocks_for(tokens_stored, B)
+    if tokens_stored % B == 0:
+        return int(table_row[blocks_used]) * B
+    return int(table_row[blocks_used - 1]) * B + (tokens_stored - (blocks_used - 1) * B)
+
+
+def _empty_tables(N, MB):
+    return np.full((N, MB), -1, dtype=np.int32)
+
+
+def _assemble(name, seed, dtype, H, D, B, NB, ctx, tables, q, logical_k, logical_v,
+              pre_k_vals, pre_v_vals, seq_blocks, pre_blocks, block_mapping,
+              new_key, new_value, slots, host, extra=None):
+    wl = Workload(name=name, seed=seed, dtype=dtype, num_heads=H, head_dim=D, block_size=B,
+                  num_blocks=NB, context_lens=ctx.astype(np.int32), block_tables=tables,
+                  scale=np.float32(1.0 / math.sqrt(D)), q=q,
+                  block_mapping=np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2),
+                  new_key=new_key, new_value=new_value,
+                  slot_mapping=np.asarray(slots, dtype=np.int64), extra=extra or {})
+    if host:
+        wl.logical_k, wl.logical_v = logical_k, logical_v
+        wl.extra["_place_after"] = (logical_k, logical_v, seq_blocks)
+        wl.extra["_place_before"] = (pre_k_vals, pre_v_vals, pre_blocks)
+    return wl
+
+
+def _build_pools(wl, key):
+    ks, vs, blocks = wl.extra[key]
+    k = np.full(wl.pool_shape, np.nan, dtype=wl.np_dtype)
+    v = np.full(wl.pool_shape, np.nan, dtype=wl.np_dtype)
+    for kv_vals, vv_vals, bl in zip(ks, vs, blocks):
+        _place(k, kv_vals, bl, wl.block_size)
+        _place(v, vv_vals, bl, wl.block_size)
+    return k, v
+
+
+def _lazy_pool(which, key):
+    attr = "_" + which
+
+    def get(self):
+        cached = self.__dict__.get(attr)
+        if cached is None:
+            if key not in self.extra:
+                return None
+            k, v = _build_pools(self, key)
+            self.__dict__["_" + which.replace("v_", "k_", 1)] = k
+            self.__dict__["_" + which.replace("k_", "v_", 1)] = v
+            cached = self.__dict__[attr]
+        return cached
+
+    def put(self, value):
+        self.__dict__[attr] = value
+
+    return property(get, put)
+
+
+def _simple(name, seed, dtype, H, D, B, ctx, NB=None, MB=None, host=True, fork_last=False):
+    """Independent sequences with scattered blocks; the step writes each
+    sequence's last token (position ctx-1).  With fork_last, the last
+    sequence is forked before the step and both copies append a token."""
+    ss = np.random.SeedSequence(seed)
+    c_place, c_q, c_kv, c_fork = ss.spawn(4)
+    npd = NP_DTYPES[dtype]
+    ctx = np.asarray(ctx, dtype=np.int64)
+    N = len(ctx)
+    rows = N + (1 if fork_last else 0)
+    q = _normal(np.random.default_rng(c_q), (rows, H, D), npd)
+    if host:
+        logical_k, logical_v = _draw_kv(c_kv.spawn(N), ctx, H, D, npd)
+    else:
+        # device fill draws the pools on the GPU; only the written tokens are
+        # drawn here (from the same per-sequence streams, first row only)
+        logical_k, logical_v = _draw_kv(c_kv.spawn(N), np.ones(N, np.int64), H, D, npd)
+    return _place_sequences(name, seed, dtype, H, D, B, ctx, q, logical_k, logical_v,
+                            np.random.default_rng(c_place), NB=NB, MB=MB, host=host,
+                            fork_rng=np.random.default_rng(c_fork) if fork_last else None)
+
+
+def _place_sequences(name, seed, dtype, H, D, B, ctx, q, logical_k, logical_v, rng_place,
+                     NB=None, MB=None, host=True, fork_rng=None):
+    npd = NP_DTYPES[dtype]
+    fork_last = fork_rng is not None
+    N = len(ctx)
+    nblks = [_blocks_for(n, B) for n in ctx]
+    used = sum(nblks) + (1 if fork_last else 0)
+    if NB is None:
+        NB = int(math.ceil(1.5 * used))
+    if MB is None:
+        MB = max(max(nblks), 1)
+    perm = rng_place.permutation(NB)
+    if used > NB:
+        raise ValueError("pool too small for the blocks in use")
+    rows = N + (1 if fork_last else 0)
+    tables = _empty_tables(rows, MB)
+    seq_blocks = []
+    cursor = 0
+    for b, nb in enumerate(nblks):
+        blocks = perm[cursor:cursor + nb]
+        cursor += nb
+        tables[b, :nb] = blocks
+        seq_blocks.append(list(blocks))
+    logical_k, logical_v = list(logical_k), list(logical_v)
+
+    # The step: every sequence appends its token at position ctx-1.
+    slots = [_next_slot(tables[b], int(ctx[b]) - 1, B) for b in range(N)]
+    new_key = np.stack([logical_k[b][-1] for b in range(N)]) if N else np.zeros((0, H, D), npd)
+    new_value = np.stack([logical_v[b][-1] for b in range(N)]) if N else np.zeros((0, H, D), npd)
+    pre_k = [lk[:-1] for lk in logical_k]
+    pre_v = [lv[:-1] for lv in logical_v]
+    pre_blocks = [list(bl) for bl in seq_blocks]
+    block_mapping = np.zeros((0, 2), dtype=np.int64)
+    all_ctx = np.asarray(ctx, dtype=np.int64)
+    extra = {}
+    if fork_last:
+        # The fork shares every block of the last sequence (refcount 2).  Its
+        # append hits the shared, partially filled last block, so that block
+        # is copied to a fresh block first and the fork writes into the copy;
+        # the original sequence then writes into its own block in place.
+        src = int(tables[N - 1, nblks[-1] - 1])
+        dst = int(perm[cursor])
+        cursor += 1
+        tables[N] = tables[N - 1]
+        tables[N, nblks[-1] - 1] = dst
+        fork_key = _normal(fork_rng, (1, H, D), npd)
+        fork_val = _normal(fork_rng, (1, H, D), npd)
+        logical_k.append(np.concatenate([logical_k[-1][:-1], fork_key]))
+        logical_v.append(np.concatenate([logical_v[-1][:-1], fork_val]))
+        seq_blocks.append(list(tables[N, :nblks[-1]]))
+        slots.append(_next_slot(tables[N], int(ctx[-1]) - 1, B))
+        new_key = np.concatenate([new_key, fork_key])
+        new_value = np.concatenate([new_value, fork_val])
+        block_mapping = np.array([[src, dst]], dtype=np.int64)
+        all_ctx = np.concatenate([all_ctx, all_ctx[-1:]])
+        extra["fork_of"] = N - 1
+    return _assemble(name, seed, dtype, H, D, B, NB, all_ctx, tables, q, logical_k, logical_v,
+                     pre_k, pre_v, seq_blocks, pre_blocks, block_mapping, new_key, new_value,
+                     slots, host, extra)
+
+
+def relayout(wl: Workload, place_seed: int, block_size: int | None = None) -> Workload:
+    """The same sequences, query and logical K/V placed afresh: a new random
+    permutation, no block shared between sequences, optionally another
+    block size.  Host fill only."""
+    if wl.logical_k is None:
+        raise ValueError("relayout needs a host-filled workload")
+    B = block_size or wl.block_size
+    return _place_sequences(wl.name + f"-relayout{place_seed}", wl.seed, wl.dtype, wl.num_heads,
+                            wl.head_dim, B, wl.context_lens.astype(np.int64), wl.q,
+                            wl.logical_k, wl.logical_v,
+                            np.random.default_rng(np.random.SeedSequence([wl.seed, 7, place_seed])))
+
+
+def config1(seed=1, host=True):
+    return _simple("tiny-fp32", seed, F32, H=2, D=64, B=16, ctx=[1, 17, 33, 50], NB=32, MB=4,
+                   host=host, fork_last=True)
+
+
+def lognormal_lengths(rng, n, median=300.0, sigma=0.9, lo=1, hi=2048):
+    z = rng.standard_normal(n)
+    return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
+
+
+def config2(seed=2, host=True, num_seqs=64, num_heads=40):
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
+    ctx = lognormal_lengths(rng, num_seqs)
+    return _simple("opt13b-layer", seed, F16, H=num_heads, D=128, B=16, ctx=ctx, MB=2048 // 16,
+                   host=host)
+
+
+def config3(seed=3, block_size=16, host=True, num_seqs=256, num_heads=40):
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
+    ctx = rng.integers(20, 200, size=num_seqs, endpoint=True)
+    return _simple(f"short-b{block_size}", seed, F16, H=num_heads, D=128, B=block_size, ctx=ctx,
+                   MB=_blocks_for(200, block_size), host=host)
+
+
+def config5(seed=5, host=False, num_seqs=32, num_heads=96, lo=4096, hi=16384):
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
+    ctx = rng.integers(lo, hi, size=num_seqs, endpoint=True)
+    return _simple("long-opt175b-layer", seed, F16, H=num_heads, D=128, B=16, ctx=ctx,
+                   MB=_blocks_for(hi, 16), host=host)
+
+
+def config4(seed=4, host=True, num_prompts=32, samples=6, num_heads=40,
+            prompt_range=(64, 512), tail_range=(1, 256)):
+    """Shared prompts with `samples` parallel samples each.  Before the step
+    the pool holds only the prompts (their blocks shared by all samples); the
+    step copies the partial last prompt block for all samples but the last
+    and then writes every tail token of every sample."""
+    H, D, B = num_heads, 128, 16
+    ss = np.random.SeedSequence(seed)
+    c_len, c_place, c_q, c_kv = ss.spawn(4)
+    rl = np.random.default_rng(c_len)
+    P = rl.integers(prompt_range[0], prompt_range[1], size=num_prompts, endpoint=True)
+    T = rl.integers(tail_range[0], tail_range[1], size=(num_prompts, samples), endpoint=True)
+    N = num_prompts * samples
+    ctx = (P[:, None] + T).reshape(-1)
+    unique = 0
+    for p in range(num_prompts):
+        pb = _blocks_for(P[p], B)
+        unique += pb + (samples - 1 if P[p] % B else 0)
+        for s in range(samples):
+            unique += _blocks_for(P[p] + T[p, s], B) - pb
+    NB = int(math.ceil(1.5 * unique))
+    perm = np.random.default_rng(c_place).permutation(NB)
+    MB = _blocks_for(prompt_range[1] + tail_range[1], B)
+    tables = _empty_tables(N, MB)
+    npd = np.float16
+    q = _normal(np.random.default_rng(c_q), (N, H, D), npd)
+    streams = [c.spawn(1 + samples) for c in c_kv.spawn(num_prompts)]
+    prompt_k, prompt_v = _draw_kv([s[0] for s in streams], P, H, D, npd)
+    tail_k, tail_v = _draw_kv([t for s in streams for t in s[1:]], T.reshape(-1), H, D, npd)
+    cursor = 0
+    logical_k, logical_v, seq_blocks = [], [], []
+    pre_k, pre_v, pre_blocks = [], [], []
+    pairs, slots, nk, nv = [], [], [], []
+    for p in range(num_prompts):
+        pk, pv = prompt_k[p], prompt_v[p]
+        pb = _blocks_for(P[p], B)
+        shared = list(perm[cursor:cursor + pb])
+        cursor += pb
+        pre_k.append(pk)
+        pre_v.append(pv)
+        pre_blocks.append(shared)
+        for s in range(samples):
+            b = p * samples + s
+            blocks = list(shared)
+            if P[p] % B and s < samples - 1:
+                dst = int(perm[cursor])
+                cursor += 1
+                pairs.append((int(shared[-1]), dst))
+                blocks[-1] = dst
+            extra_blocks = _blocks_for(P[p] + T[p, s], B) - pb
+            blocks += list(perm[cursor:cursor + extra_blocks])
+            cursor += extra_blocks
+            tables[b, :len(blocks)] = blocks
+            tk, tv = tail_k[b], tail_v[b]
+            logical_k.append(np.concatenate([pk, tk]))
+            logical_v.append(np.concatenate([pv, tv]))
+            seq_blocks.append(blocks)
+            for i in range(int(T[p, s])):
+                slots.append(_next_slot(tables[b], int(P[p]) + i, B))
+            nk.append(tk)
+            nv.append(tv)
+    assert cursor == unique
+    extra = {"prompt_lens": P, "tail_lens": T, "samples": samples, "unique_blocks": unique}
+    return _assemble("shared-prefix-cow", seed, F16, H, D, B, NB, ctx, tables, q,
+                     logical_k, logical_v, pre_k, pre_v, seq_blocks, pre_blocks,
+                     np.array(pairs, dtype=np.int64).reshape(-1, 2),
+                     np.concatenate(nk), np.concatenate(nv), slots, host, extra)
+
+
+# Host fill: pools before the step (k_pool_pre, v_pool_pre) and after it
+# (k_pool, v_pool), [NB][H][B][D], built on first use.
+Workload.k_pool_pre = _lazy_pool("k_pool_pre", "_place_before")
+Workload.v_pool_pre = _lazy_pool("v_pool_pre", "_place_before")
+Workload.k_pool = _lazy_pool("k_pool", "_place_after")
+Workload.v_pool = _lazy_pool("v_pool", "_place_after")
+
+
+def make(config: int, **kw) -> Workload:
+    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[config](**kw)
+
+
+# ---------------------------------------------------------------------------
+# Device fill: the same metadata, with pool contents drawn on the GPU by
+# torch's seeded generator (for sizes where drawing on the host is too slow).
+# Logical order is not preserved; every live slot holds N(0,1), every other
+# slot NaN.
+# ---------------------------------------------------------------------------
+
+def live_rows(wl: Workload):
+    """(block ids, number of filled rows) for every block in use."""
+    ids, filled = [], []
+    B = wl.block_size
+    for b in range(wl.num_seqs):
+        n = int(wl.context_lens[b])
+        nb = _blocks_for(n, B)
+        ids.append(wl.block_tables[b, :nb].astype(np.int64))
+        f = np.full(nb, B, dtype=np.int64)
+        if nb:
+            f[-1] = n - (nb - 1) * B
+        filled.append(f)
+    ids = np.concatenate(ids) if ids else np.zeros(0, np.int64)
+    filled = np.concatenate(filled) if filled else np.zeros(0, np.int64)
+    # blocks shared by several sequences appear once
+    uniq, first = np.unique(ids, return_index=True)
+    return uniq, filled[first]
+
+
+def device_pools(wl: Workload, device, seed_offset=0, chunk_blocks=2048):
+    """Allocate and fill (k_pool, v_pool) on `device` with torch's RNG."""
+    import torch
+    tdt = torch.float16 if wl.dtype == F16 else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(wl.seed) * 1000003 + seed_offset)
+    shape = wl.pool_shape
+    pools = []
+    ids, filled = live_rows(wl)
+    ids_t = torch.as_tensor(ids, device=device)
+    filled_t = torch.as_tensor(filled, device=device)
+    row = torch.arange(wl.block_size, device=device)
+    for _ in range(2):
+        pool = torch.full(shape, float("nan"), dtype=tdt, device=device)
+        for c0 in range(0, len(ids), chunk_blocks):
+            sel = ids_t[c0:c0 + chunk_blocks]
+            vals = torch.randn((len(sel),) + shape[1:], generator=gen, device=device,
+                               dtype=torch.float32).to(tdt)
+            keep = (row[None, :] < filled_t[c0:c0 + chunk_blocks, None])  # [n][B]
+            vals = torch.where(keep[:, None, :, None], vals, torch.full_like(vals, float("nan")))
+            pool[sel] = vals
+        pools.append(pool)
+    return pools[0], pools[1]
