@@ -1,0 +1,170 @@
+/*
+ * pa.h -- paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over three HIP kernel families: single-query decode attention over
+ * a KV cache stored in fixed-size blocks at scattered physical locations
+ * (PagedAttention), the per-step write of new tokens' K/V into their slots,
+ * and the block-granular copy-on-write copy.  Source: Kwon et al., "Efficient
+ * Memory Management for Large Language Model Serving with PagedAttention"
+ * (2023), as summarised on three web pages:
+ *   [wywy]  wywy.jp reading notes,
+ *   [zhai]  zhaifeiyue.github.io structured summary,
+ *   [rice]  ricepunchb.github.io "KV Cache Optimization" notes.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every pointer argument is device memory owned by the caller (except
+ *    `stream`, a hipStream_t, and the return of pa_status_string).  The
+ *    library allocates nothing, frees nothing and keeps no state between
+ *    calls.  It is thread-safe.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the default stream);
+ *    no call synchronises.  Buffers must stay valid until the work completes.
+ *  - Element type codes: PA_F16 (IEEE binary16) or PA_F32.  Query, pools,
+ *    keys, values and output of one call share the element type; attention
+ *    arithmetic is fp32.
+ *  - KV pool layout (both pools): [num_blocks][num_heads][block_size][head_dim]
+ *    row-major, so one (block, head) tile is block_size*head_dim contiguous
+ *    elements and one block, all heads, is num_heads*block_size*head_dim
+ *    contiguous elements.  K and V live in separate pools addressed by one
+ *    block table ([wywy] Keyword "PagedAttention": K and V in separate blocks).
+ *  - Token t (0-based) of sequence b lives in logical block t / block_size at
+ *    offset t % block_size; its physical block is block_tables[b][t /
+ *    block_size] ([rice] 3.2 "address translation": block index, block
+ *    offset, physical address; [wywy] Keyword "Block table").
+ *  - Floating-point arrays must be 16-byte aligned.
+ *  - Return value: PA_OK (0) or a negative PA_ERR_* code.  On any error other
+ *    than PA_ERR_HIP nothing was enqueued.  Only scalars and pointers are
+ *    validated on the host; device array contents (table entries, slots,
+ *    copy pairs, context lengths) are preconditions.  Kernels skip table
+ *    entries, slots and copy pairs that fall outside the pool rather than
+ *    access memory out of bounds (a decode row that meets such an entry is
+ *    written as NaN), and clamp context lengths to [0, max_context_len].
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* a size is out of range, or a pointer misaligned */
+#define PA_ERR_UNSUPPORTED (-3) /* head_dim, block_size or dtype not compiled in */
+#define PA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+#define PA_ERR_HIP (-5)         /* the HIP runtime rejected a launch */
+
+/* Element types. */
+#define PA_F16 0
+#define PA_F32 1
+
+/* Supported sizes: head_dim in {64, 128}; block_size in {8, 16, 32, 64}. */
+
+/* Partition length used when pa_decode is given partition_size == 0. */
+#define PA_DEFAULT_PARTITION 512
+
+/*
+ * Bytes of workspace pa_decode needs for this batch shape:
+ * ceil(max_context_len / P) partitions per (sequence, head), where P is the
+ * partition length (partition_size, or PA_DEFAULT_PARTITION when 0).  Returns
+ * 0 when every context fits in one partition (no workspace needed) and
+ * (size_t)-1 for invalid arguments.
+ */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                 int max_context_len, int partition_size);
+
+/*
+ * Single-query paged decode attention ([zhai] "method" paragraph, the
+ * block-wise equation for A_ij and o_i; [rice] 3.3: per-block scores, the
+ * softmax completed by a final reduction; [wywy] WHERE: the kernel fetches
+ * each needed block separately).
+ *
+ * For every sequence b < num_seqs and head h < num_heads, with
+ * n = context_lens[b]:
+ *     s_t      = scale * dot(q[b][h][:], K[phys(b,t)][h][t % B][:]),  t < n
+ *     out[b][h][:] = sum_t softmax(s)_t * V[phys(b,t)][h][t % B][:]
+ * where phys(b,t) = block_tables[b][t / B].  Slots of the last block at
+ * offsets >= the filled count are not read into the result (they may hold
+ * anything, NaN included).  n == 0 gives a zero row.
+ *
+ *   out            [num_seqs][num_heads][head_dim], element type dtype (written)
+ *   q              [num_seqs][num_heads][head_dim], dtype
+ *   k_pool, v_pool [num_blocks][num_heads][block_size][head_dim], dtype
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]; entries below
+ *                  ceil(n / block_size) must lie in [0, num_blocks); later
+ *                  entries are never read
+ *   context_lens   int32 [num_seqs], each in [0, max_context_len]
+ *   max_context_len host-side bound on context_lens, at most
+ *                  max_blocks_per_seq * block_size; sizes the launch grid, so
+ *                  the host never reads device data
+ *   scale          multiplier of the dot products (usually 1/sqrt(head_dim))
+ *   partition_size tokens per context partition, a multiple of 16 in
+ *                  [16, 65536], or 0 for PA_DEFAULT_PARTITION.  Contexts longer
+ *                  than one partition are split across workgroups and merged
+ *                  exactly (max/sum rescaling).
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes (256-byte aligned), or NULL when that is 0: the
+ *                  per-partition partial results (max, sum, unnormalised
+ *                  output) of rows longer than one partition.  Contents on
+ *                  entry are ignored; concurrent calls must not share one
+ *                  workspace.
+ *
+ * Launches one kernel, plus a small merge kernel when max_context_len
+ * exceeds one partition.  Workgroups own (head, sequence, partition); rows
+ * that fit one partition are finished by the first kernel.
+ */
+int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+              const int32_t *block_tables, const int32_t *context_lens,
+              int num_seqs, int num_heads, int head_dim, int block_size,
+              int num_blocks, int max_blocks_per_seq, int max_context_len,
+              float scale, int dtype, int partition_size,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Store each new token's K and V rows, all heads, in its slot ([wywy]
+ * Keyword "autoregressive generation phase": each step creates K/V only for
+ * the new token; [zhai] "KV Cache Manager": a new block is taken only when
+ * the previous one is full).  For token i with slot = slot_mapping[i] >= 0:
+ *     K[slot / B][h][slot % B][:] = key[i][h][:]   for every head h
+ *     V[slot / B][h][slot % B][:] = value[i][h][:]
+ * Bit copies.  A negative slot skips the token (padding).  Slots must be
+ * distinct (two tokens into one slot race) and below num_blocks * block_size.
+ *
+ *   key, value    [num_tokens][num_heads][head_dim], dtype
+ *   k_pool, v_pool pools as for pa_decode (written)
+ *   slot_mapping  int64 [num_tokens], slot = physical_block * block_size + offset
+ */
+int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
+                const int64_t *slot_mapping, int num_tokens, int num_heads,
+                int head_dim, int block_size, int num_blocks, int dtype,
+                void *stream);
+
+/*
+ * Block-granular copy-on-write copy ([wywy] WHERE, parallel sampling: on a
+ * write to a block whose reference count exceeds 1, a new block is allocated
+ * and the block engine copies the old block's contents into it; [zhai]
+ * memory-management table, "Copy-on-Write": one block per copy).  For each
+ * pair i, the whole block src = block_mapping[2i] (every head, every offset)
+ * is copied onto dst = block_mapping[2i+1], in both pools.  Bit copies.  One
+ * source may feed several destinations; destinations must be distinct and
+ * must not appear as sources.
+ *
+ *   k_pool, v_pool pools as for pa_decode (read and written)
+ *   block_mapping int64 [num_pairs][2] (src, dst), device memory
+ */
+int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
+                   int num_pairs, int num_heads, int head_dim, int block_size,
+                   int num_blocks, int dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

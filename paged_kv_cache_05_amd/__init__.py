@@ -1,0 +1,180 @@
+"""Paged decode attention for MI355X: Python binding of ``libpa.so``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/pa.h``.  Tensors are torch
+device tensors (torch supplies device memory and streams); the functions
+carry the C names:
+
+* :func:`pa_decode` -- single-query decode attention over block pools
+  addressed through per-sequence block tables,
+* :func:`pa_write_kv` -- store the new tokens' K/V rows in their slots,
+* :func:`pa_copy_blocks` -- copy-on-write copy of whole physical blocks,
+* :func:`pa_decode_workspace_bytes`, :func:`pa_status_string`.
+
+If ``libpa.so`` has not been built, every call raises :class:`PAError`;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libpa.so")
+
+PA_OK = 0
+PA_F16 = 0
+PA_F32 = 1
+PA_DEFAULT_PARTITION = 512
+
+# Every symbol include/pa.h declares.
+EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_write_kv", "pa_copy_blocks",
+           "pa_status_string")
+
+
+class PAError(RuntimeError):
+    """A C-ABI call returned an error, or the library is missing."""
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libpa.so (built in-tree by ``python -m paged_kv_cache_05_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise PAError(f"{LIBRARY} is not built; run `python -m paged_kv_cache_05_amd._build` "
+                      "(there is no fallback path)")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                              f32, i32, i32, vp, sz, vp]
+    lib.pa_decode.restype = i32
+    lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_write_kv.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return library().pa_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != PA_OK:
+        raise PAError(f"{what}: {pa_status_string(rc)} ({rc})")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return PA_F16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise PAError(f"unsupported element type {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PAError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PAError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                              partition_size=0) -> int:
+    n = library().pa_decode_workspace_bytes(int(num_seqs), int(num_heads), int(head_dim),
+                                            int(max_context_len), int(partition_size))
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError("pa_decode_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def new_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size=0,
+                  device="cuda"):
+    """A workspace of the size pa_decode needs (None when none is needed)."""
+    import torch
+    n = pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+              partition_size=0, workspace=None, stream=None):
+    """out[N][H][D] = paged decode attention of q[N][H][D] over the pools.
+
+    k_pool/v_pool: [num_blocks][H][block_size][D]; block_tables int32
+    [N][max_blocks_per_seq]; context_lens int32 [N]; max_context_len: host
+    int >= every context length; workspace: from :func:`new_workspace`.
+    """
+    import torch
+    N, H, D = q.shape
+    NB, H2, B, D2 = k_pool.shape
+    if (H2, D2) != (H, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise PAError("pool shape does not match q")
+    if tuple(out.shape) != (N, H, D) or out.dtype != q.dtype:
+        raise PAError("out must match q in shape and type")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise PAError("q and pools must share one element type")
+    if block_tables.dim() != 2 or block_tables.shape[0] != N or tuple(context_lens.shape) != (N,):
+        raise PAError("block_tables / context_lens do not match the batch")
+    ws_ptr = _dev(workspace, "workspace", torch.uint8)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    rc = library().pa_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        N, H, D, B, NB, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
+        int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "pa_decode")
+    return out
+
+
+def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
+    """Store key/value [T][H][D] rows at slot_mapping (int64 [T]) in the pools."""
+    import torch
+    T, H, D = key.shape
+    NB, H2, B, D2 = k_pool.shape
+    if (H2, D2) != (H, D) or tuple(value.shape) != tuple(key.shape) or \
+            tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(slot_mapping.shape) != (T,):
+        raise PAError("pa_write_kv: shapes do not match")
+    if not (key.dtype == value.dtype == k_pool.dtype == v_pool.dtype):
+        raise PAError("pa_write_kv: key, value and pools must share one element type")
+    rc = library().pa_write_kv(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T, H, D, B, NB, _dtype_code(key),
+        _stream(stream))
+    _check(rc, "pa_write_kv")
+
+
+def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
+    """Copy whole blocks (src, dst) = block_mapping[i] (int64 [P][2]) in both pools."""
+    import torch
+    NB, H, B, D = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or v_pool.dtype != k_pool.dtype:
+        raise PAError("pa_copy_blocks: pools differ")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise PAError("pa_copy_blocks: block_mapping must be [P][2]")
+    rc = library().pa_copy_blocks(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0], H, D, B, NB,
+        _dtype_code(k_pool), _stream(stream))
+    _check(rc, "pa_copy_blocks")

@@ -1,0 +1,151 @@
+// C ABI of libpa.so: argument validation and dispatch to the kernels.  The
+// contract (shapes, layouts, ownership, errors) is documented in
+// include/pa.h; this file checks scalars and pointers only and never reads
+// device memory.
+#include <math.h>
+
+#include "../../include/pa.h"
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kMaxPartition = 65536;
+constexpr int kGridYZ = 65535;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dtype) {
+  if (dtype == PA_F16) return 2;
+  if (dtype == PA_F32) return 4;
+  return 0;
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+bool supported_block(int b) { return b == 8 || b == 16 || b == 32 || b == 64; }
+
+// Shared checks of the pool geometry.  0 or an error code.
+int check_pool(int num_heads, int head_dim, int block_size, int num_blocks, int dtype) {
+  if (!elem_bytes(dtype) || !supported_head_dim(head_dim) || !supported_block(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int effective_partition(int partition_size) {
+  return partition_size == 0 ? PA_DEFAULT_PARTITION : partition_size;
+}
+
+bool valid_partition(int part) { return part >= 16 && part <= kMaxPartition && part % 16 == 0; }
+
+int num_partitions(int max_context_len, int part) {
+  return max_context_len <= 0 ? 1 : (max_context_len + part - 1) / part;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range or a pointer is misaligned";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                 int partition_size) {
+  const int part = effective_partition(partition_size);
+  if (num_seqs < 0 || num_heads <= 0 || !supported_head_dim(head_dim) || max_context_len < 0 ||
+      !valid_partition(part))
+    return (size_t)-1;
+  const int np = num_partitions(max_context_len, part);
+  if (np <= 1 || num_seqs == 0) return 0;
+  return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, np).total;
+}
+
+int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+              const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+              int num_heads, int head_dim, int block_size, int num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+              int partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  const int part = effective_partition(partition_size);
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
+      !valid_partition(part) || !isfinite(scale) || num_seqs > kGridYZ || num_heads > kGridYZ ||
+      num_partitions(max_context_len, part) > kGridYZ)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+    return PA_ERR_SHAPE;
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_heads = num_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.partition_size = part;
+  p.num_partitions = num_partitions(max_context_len, part);
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  if (p.num_partitions > 1) {
+    const pa::WorkspaceLayout w =
+        pa::decode_workspace_layout(num_seqs, num_heads, head_dim, p.num_partitions);
+    if (!workspace) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_SHAPE;
+    char *base = static_cast<char *>(workspace);
+    p.part_ml = reinterpret_cast<float2 *>(base + w.ml_off);
+    p.part_o = reinterpret_cast<float *>(base + w.o_off);
+  }
+  return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
+                const int64_t *slot_mapping, int num_tokens, int num_heads, int head_dim,
+                int block_size, int num_blocks, int dtype, void *stream) {
+  int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return PA_ERR_SHAPE;
+  return from_hip(pa::launch_write_kv(key, value, k_pool, v_pool, slot_mapping, num_tokens,
+                                      num_heads, head_dim * elem_bytes(dtype), block_size,
+                                      num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping, int num_pairs,
+                   int num_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                   void *stream) {
+  int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)block_mapping & 7u))
+    return PA_ERR_SHAPE;
+  const size_t block_bytes = (size_t)num_heads * block_size * head_dim * elem_bytes(dtype);
+  return from_hip(pa::launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
+                                         num_blocks, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

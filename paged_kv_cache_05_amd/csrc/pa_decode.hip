@@ -1,0 +1,457 @@
+// Paged single-query decode attention for gfx950 (CDNA 4).
+//
+// Computes, for every (sequence b, head h), attention of the one query token
+// over the sequence's cached keys and values, which sit in fixed-size blocks
+// scattered through two pools (K and V) and are found through the
+// sequence's block table: the block-wise form of attention in the
+// zhaifeiyue.github.io summary of Kwon et al. (PagedAttention), "method"
+// paragraph, equation for A_ij and o_i, completed "by a final reduction" as
+// ricepunchb.github.io section 3.3 puts it.
+//
+// Design (MI355X: wave64, 16-byte vector loads, DPP, HBM-bound):
+//  * One workgroup of W waves per (head, sequence, context partition).  A
+//    partition is `partition_size` tokens; each wave takes every W-th
+//    16-token tile of it.
+//  * A token row of K or V (head_dim elements) is read as 16-byte chunks by
+//    a group of lanes: at fp16/head_dim 128 one row is 256 bytes = 16 lanes,
+//    so one wave load covers 4 consecutive tokens and a 16-token tile is 4
+//    loads of K and 4 of V, each 1 KiB contiguous inside one block.
+//  * The physical block of a tile comes from one scalar load of the block
+//    table entry (block index = token / B, offset = token % B), so address
+//    translation costs one s_load per tile and no vector work.
+//  * q.k per token: v_dot2 (fp16 pairs into fp32) on the lane's chunk, then a
+//    DPP row reduction over the lanes of the token (quad_perm, half-mirror,
+//    mirror).  Every lane of the row ends up holding the token's score.
+//  * Online softmax in base 2 (scale * log2 e folded into one multiply).
+//    Each lane row keeps its own running max / sum / accumulator for the
+//    tokens it sees (tokens congruent to it modulo the row count), so the hot
+//    loop has no cross-row traffic; rows and waves are merged once through
+//    LDS at the end with the usual max/sum rescaling.
+//  * Masking of the ragged last tile is a select on scores and values, never
+//    a multiply by zero, so whatever sits in unused slots (NaN included)
+//    cannot reach the result.
+//  * A row whose context fits one partition is finished in the first pass.
+//    Longer rows are split across workgroups; each writes (max, sum,
+//    unnormalised output) to the workspace and a second, small kernel merges
+//    them with max/sum rescaling.  (Merging inside the first kernel would
+//    need device-scope release/acquire fences, which on this multi-L2 part
+//    write back and invalidate the L2 per workgroup.)
+//  * No MFMA: one query row per (sequence, head) makes q.K and p.V
+//    matrix-vector products, about one flop per byte moved.
+#include <math.h>
+
+#include <type_traits>
+
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+union Chunk {  // one 16-byte vector load
+  uint4 u;
+  uint32_t w[4];
+};
+
+template <typename T, int D>
+struct Geometry {
+  static constexpr int kElemBytes = sizeof(T);
+  static constexpr int kPerChunk = 16 / kElemBytes;     // elements per 16-byte chunk
+  static constexpr int kChunksPerRow = D / kPerChunk;   // chunks per token row
+  static constexpr int kLanesPerToken = kChunksPerRow < 16 ? kChunksPerRow : 16;
+  static constexpr int kChunksPerLane = kChunksPerRow / kLanesPerToken;
+  static constexpr int kTokensPerGroup = 64 / kLanesPerToken;  // tokens per wave load
+  static constexpr int kTile = 16;                              // tokens per wave step
+  static constexpr int kGroups = kTile / kTokensPerGroup;
+  static constexpr int kAcc = kChunksPerLane * kPerChunk;     // output elements per lane
+  static_assert(kLanesPerToken == 8 || kLanesPerToken == 16, "row reduction covers 8 or 16 lanes");
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl,
+                                                            0xF, 0xF, true));
+}
+
+// Sum over each aligned group of kLanes (8 or 16) lanes; every lane of the
+// group receives the total.
+template <int kLanes>
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: pairs
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: quads
+  v += dpp<0x141>(v);  // row_half_mirror: eights
+  if constexpr (kLanes == 16) v += dpp<0x140>(v);  // row_mirror: sixteens
+  return v;
+}
+
+__device__ __forceinline__ Chunk load_chunk(const char *p) {
+  Chunk c;
+  c.u = *reinterpret_cast<const uint4 *>(p);
+  return c;
+}
+
+__device__ __forceinline__ float dot_chunk(const Chunk &q, const Chunk &k, float acc, _Float16) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.w[j]),
+                                 __builtin_bit_cast(half2_t, k.w[j]), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float dot_chunk(const Chunk &q, const Chunk &k, float acc, float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_fmaf(__builtin_bit_cast(float, q.w[j]), __builtin_bit_cast(float, k.w[j]), acc);
+  return acc;
+}
+
+__device__ __forceinline__ void axpy_chunk(float *acc, float p, const Chunk &v, _Float16) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2_t h = __builtin_bit_cast(half2_t, v.w[j]);
+    acc[2 * j] = __builtin_fmaf(p, (float)h.x, acc[2 * j]);
+    acc[2 * j + 1] = __builtin_fmaf(p, (float)h.y, acc[2 * j + 1]);
+  }
+}
+
+__device__ __forceinline__ void axpy_chunk(float *acc, float p, const Chunk &v, float) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc[j] = __builtin_fmaf(p, __builtin_bit_cast(float, v.w[j]), acc[j]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int D>
+struct Tile {
+  using G = Geometry<T, D>;
+  Chunk k[G::kGroups][G::kChunksPerLane];
+  Chunk v[G::kGroups][G::kChunksPerLane];
+};
+
+// Per-lane-row softmax state.
+template <int kAcc>
+struct RowState {
+  float m, l;
+  float acc[kAcc];
+};
+
+template <typename T, int D, int B, int W>
+__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
+  using G = Geometry<T, D>;
+  constexpr int kStates = W * G::kTokensPerGroup;
+  constexpr int kLPT = G::kLanesPerToken;
+  constexpr int kTPG = G::kTokensPerGroup;
+  __shared__ float s_m[kStates];
+  __shared__ float s_l[kStates];
+  __shared__ float s_o[kStates][D];
+
+  // Partition index is the slowest grid dimension: every partition-0
+  // workgroup (always busy) is dispatched before those of later
+  // partitions, many of which find their sequence too short and exit.
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
+  const int H = p.num_heads;
+  const size_t row = (size_t)b * H + h;
+
+  int ctx = p.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
+  T *out_row = reinterpret_cast<T *>(p.out) + row * D;
+  if (ctx == 0) {
+    if (part == 0)
+      for (int d = threadIdx.x; d < D; d += 64 * W) out_row[d] = T(0);
+    return;
+  }
+  const int P = p.partition_size;
+  const int tok0 = part * P;
+  if (tok0 >= ctx) return;
+  const int tok_end = min(ctx, tok0 + P);
+  const int n_parts = (ctx + P - 1) / P;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane % kLPT;   // which 16-byte chunk(s) of a token row
+  const int trow = lane / kLPT;  // which token of a 4- or 8-token group
+
+  Chunk qc[G::kChunksPerLane];
+  {
+    const char *qp = reinterpret_cast<const char *>(p.q) + row * D * sizeof(T);
+#pragma unroll
+    for (int k = 0; k < G::kChunksPerLane; ++k) qc[k] = load_chunk(qp + (col + k * kLPT) * 16);
+  }
+
+  const int32_t *table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const size_t block_bytes = (size_t)H * B * D * sizeof(T);
+  const size_t lane_off = ((size_t)h * B + trow) * D * sizeof(T) + (size_t)col * 16;
+  const char *kbase = reinterpret_cast<const char *>(p.k_pool) + lane_off;
+  const char *vbase = reinterpret_cast<const char *>(p.v_pool) + lane_off;
+  const unsigned num_blocks = (unsigned)p.num_blocks;
+  bool bad = false;
+
+  // Load the 16-token tile starting at logical token ts.  With kCheck,
+  // groups at or past tok_end are not loaded (their table entries may not
+  // exist); full tiles skip the check.
+  auto fetch = [&](Tile<T, D> &tile, int ts, auto check_tag) {
+    constexpr bool kCheck = decltype(check_tag)::value;
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) {
+      const int gs = ts + g * kTPG;
+      int lb, off;
+      if constexpr (B >= 16) {
+        lb = ts / B;
+        off = ts % B + g * kTPG;
+      } else {
+        lb = gs / B;
+        off = gs % B;
+      }
+      if (!kCheck || gs < tok_end) {
+        const int phys = table[lb];
+        const bool ok = (unsigned)phys < num_blocks;
+        bad |= !ok;
+        const size_t boff = (size_t)(ok ? phys : 0) * block_bytes + (size_t)off * D * sizeof(T);
+#pragma unroll
+        for (int k = 0; k < G::kChunksPerLane; ++k) {
+          tile.k[g][k] = load_chunk(kbase + boff + k * kLPT * 16);
+          tile.v[g][k] = load_chunk(vbase + boff + k * kLPT * 16);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < G::kChunksPerLane; ++k) {
+          tile.k[g][k].u = make_uint4(0, 0, 0, 0);
+          tile.v[g][k].u = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  RowState<G::kAcc> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::kAcc; ++i) st.acc[i] = 0.f;
+
+  // Fold one tile into the row state.  kMask: the tile may hold tokens at or
+  // past tok_end, which are excluded by select.
+  auto consume = [&](Tile<T, D> &tile, int ts, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    float s[G::kGroups];
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < G::kChunksPerLane; ++k) d = dot_chunk(qc[k], tile.k[g][k], d, T());
+      s[g] = row_sum<kLPT>(d) * p.scale_log2;
+    }
+    if constexpr (kMask) {
+#pragma unroll
+      for (int g = 0; g < G::kGroups; ++g) {
+        const bool valid = ts + g * kTPG + trow < tok_end;
+        s[g] = valid ? s[g] : -INFINITY;
+#pragma unroll
+        for (int k = 0; k < G::kChunksPerLane; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tile.v[g][k].w[j] = valid ? tile.v[g][k].w[j] : 0u;
+      }
+    }
+    float mx = st.m;
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) mx = fmaxf(mx, s[g]);
+    // A row that has seen no valid token keeps m = -inf; use 0 as the
+    // reference so that no -inf - -inf appears.
+    const float mu = (kMask && mx == -INFINITY) ? 0.f : mx;
+    const float alpha = fast_exp2(st.m - mu);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < G::kAcc; ++i) st.acc[i] *= alpha;
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) {
+      const float pg = fast_exp2(s[g] - mu);
+      st.l += pg;
+#pragma unroll
+      for (int k = 0; k < G::kChunksPerLane; ++k)
+        axpy_chunk(st.acc + k * G::kPerChunk, pg, tile.v[g][k], T());
+    }
+    st.m = mx;
+  };
+
+  const int span = tok_end - tok0;
+  const int nfull = span / G::kTile;
+  {
+    // Full tiles of this wave: t = wave, wave + W, ...  Two tile buffers in
+    // ping-pong; each step issues the next tile's loads before consuming the
+    // current one, and the issue is unconditional inside each branch so the
+    // wait before a consume covers only that tile's loads.
+    const int iters = nfull > wave ? (nfull - wave + W - 1) / W : 0;
+    Tile<T, D> ta, tb;
+    int t = wave;
+    if (iters > 0) fetch(ta, tok0 + t * G::kTile, std::false_type());
+    for (int i = 0; i < iters; i += 2) {
+      if (i + 1 < iters) {
+        fetch(tb, tok0 + (t + W) * G::kTile, std::false_type());
+        consume(ta, tok0 + t * G::kTile, std::false_type());
+      } else {
+        consume(ta, tok0 + t * G::kTile, std::false_type());
+        break;
+      }
+      t += W;
+      if (i + 2 < iters) {
+        fetch(ta, tok0 + (t + W) * G::kTile, std::false_type());
+        consume(tb, tok0 + t * G::kTile, std::false_type());
+      } else {
+        consume(tb, tok0 + t * G::kTile, std::false_type());
+        break;
+      }
+      t += W;
+    }
+    // Ragged last tile.
+    if (nfull * G::kTile < span && wave == nfull % W) {
+      const int ts = tok0 + nfull * G::kTile;
+      fetch(ta, ts, std::true_type());
+      consume(ta, ts, std::true_type());
+    }
+  }
+  if (bad) st.l = NAN;  // a table entry outside the pool poisons the row
+
+  // Merge the W * kTPG row states of this workgroup.
+  {
+    const int sidx = wave * kTPG + trow;
+    if (col == 0) {
+      s_m[sidx] = st.m;
+      s_l[sidx] = st.l;
+    }
+#pragma unroll
+    for (int k = 0; k < G::kChunksPerLane; ++k)
+#pragma unroll
+      for (int i = 0; i < G::kPerChunk; ++i)
+        s_o[sidx][(col + k * kLPT) * G::kPerChunk + i] = st.acc[k * G::kPerChunk + i];
+  }
+  __syncthreads();
+
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kStates; ++s) M = fmaxf(M, s_m[s]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kStates; ++s) {
+    const float ms = s_m[s];
+    lsum += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_l[s];
+  }
+
+  if (n_parts == 1) {
+    for (int d = threadIdx.x; d < D; d += 64 * W) {
+      float o = 0.f;
+#pragma unroll
+      for (int s = 0; s < kStates; ++s) {
+        const float ms = s_m[s];
+        o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_o[s][d];
+      }
+      out_row[d] = T(o / lsum);
+    }
+    return;
+  }
+
+  // Several partitions: publish this one's partial result for the merge pass.
+  const int NP = p.num_partitions;
+  float *po = p.part_o + (row * NP + part) * D;
+  for (int d = threadIdx.x; d < D; d += 64 * W) {
+    float o = 0.f;
+#pragma unroll
+    for (int s = 0; s < kStates; ++s) {
+      const float ms = s_m[s];
+      o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_o[s][d];
+    }
+    po[d] = o;
+  }
+  if (threadIdx.x == 0) p.part_ml[row * NP + part] = make_float2(M, lsum);
+}
+
+// Second pass, rows with several partitions only: out = sum_p w_p o_p /
+// sum_p w_p l_p with w_p = 2^(m_p - max_p m_p).  One workgroup per
+// (head, sequence); the partition results come from the first pass, made
+// visible by the kernel boundary.
+template <typename T, int D>
+__global__ void __launch_bounds__(D) merge_kernel(const DecodeParams p) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const size_t row = (size_t)b * p.num_heads + h;
+  int ctx = p.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
+  const int P = p.partition_size;
+  const int n_parts = (ctx + P - 1) / P;
+  if (n_parts <= 1) return;  // written by the first pass
+  const int NP = p.num_partitions;
+  const float2 *ml = p.part_ml + row * NP;
+  float gM = -INFINITY;
+  for (int q = 0; q < n_parts; ++q) gM = fmaxf(gM, ml[q].x);
+  const float *po = p.part_o + row * NP * D;
+  const int d = threadIdx.x;
+  float num = 0.f, den = 0.f;
+  for (int q = 0; q < n_parts; ++q) {
+    const float2 mlq = ml[q];
+    const float w = mlq.x == -INFINITY ? 0.f : fast_exp2(mlq.x - gM);
+    num += w * po[(size_t)q * D + d];
+    den += w * mlq.y;
+  }
+  reinterpret_cast<T *>(p.out)[row * D + d] = T(num / den);
+}
+
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8
+#endif
+
+template <typename T, int D, int B>
+hipError_t launch_typed(const DecodeParams &p, int num_seqs, hipStream_t stream) {
+  constexpr int W = PA_DECODE_WAVES;  // waves per workgroup
+  const dim3 grid(p.num_heads, num_seqs, p.num_partitions);
+  decode_kernel<T, D, B, W><<<grid, 64 * W, 0, stream>>>(p);
+  if (p.num_partitions > 1)
+    merge_kernel<T, D><<<dim3(p.num_heads, num_seqs), D, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_block(const DecodeParams &p, int num_seqs, int block_size, hipStream_t s) {
+  switch (block_size) {
+    case 8: return launch_typed<T, D, 8>(p, num_seqs, s);
+    case 16: return launch_typed<T, D, 16>(p, num_seqs, s);
+    case 32: return launch_typed<T, D, 32>(p, num_seqs, s);
+    case 64: return launch_typed<T, D, 64>(p, num_seqs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_dim(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
+                      hipStream_t s) {
+  switch (head_dim) {
+    case 64: return launch_block<T, 64>(p, num_seqs, block_size, s);
+    case 128: return launch_block<T, 128>(p, num_seqs, block_size, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_dim,
+                                        int num_partitions) {
+  WorkspaceLayout w{};
+  const size_t rows = (size_t)num_seqs * num_heads;
+  const size_t parts = rows * (size_t)num_partitions;
+  w.ml_off = 0;
+  w.o_off = align256(parts * sizeof(float2));
+  w.total = w.o_off + align256(parts * (size_t)head_dim * sizeof(float));
+  return w;
+}
+
+hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
+                         int dtype, hipStream_t stream) {
+  if (dtype == 0) return launch_dim<_Float16>(p, num_seqs, head_dim, block_size, stream);
+  if (dtype == 1) return launch_dim<float>(p, num_seqs, head_dim, block_size, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

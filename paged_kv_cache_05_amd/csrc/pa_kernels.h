@@ -1,0 +1,49 @@
+// Internal interface between the C ABI (pa_api.hip) and the kernel files.
+// Not installed; the public contract is include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything the decode kernel reads besides its template parameters.
+struct DecodeParams {
+  void *out;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  int num_heads;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int max_context_len;
+  int partition_size;   // tokens per partition, multiple of 16
+  int num_partitions;   // ceil(max_context_len / partition_size)
+  float scale_log2;     // scale * log2(e): scores are kept in base 2
+  float2 *part_ml;      // [num_seqs * num_heads][num_partitions] (max, sum)
+  float *part_o;        // [num_seqs * num_heads][num_partitions][head_dim]
+};
+
+// Workspace carve-up shared by the size query and the launch.
+struct WorkspaceLayout {
+  size_t ml_off, o_off, total;
+};
+WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_dim,
+                                        int num_partitions);
+
+// dtype: 0 = f16, 1 = f32.  Returns the launch status.
+hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
+                         int dtype, hipStream_t stream);
+
+hipError_t launch_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
+                           const int64_t *slot_mapping, int num_tokens, int num_heads,
+                           int row_bytes, int block_size, int num_blocks, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
+                              int num_pairs, size_t block_bytes, int num_blocks,
+                              hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: libpa.so loads, exports every function
+include/pa.h declares, and rejects bad arguments on the host before any
+launch.  Validation calls pass fake (never dereferenced) device addresses,
+so they only run where no GPU is visible."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports(pa):
+    assert declared_functions() == sorted(pa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(pa):
+    lib = pa.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pa_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_constants_match_binding(pa):
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (PA_\w+) \(?(-?\d+)\)?", text))
+    assert int(consts["PA_OK"]) == pa.PA_OK
+    assert int(consts["PA_F16"]) == pa.PA_F16 and int(consts["PA_F32"]) == pa.PA_F32
+    assert int(consts["PA_DEFAULT_PARTITION"]) == pa.PA_DEFAULT_PARTITION
+
+
+def test_status_strings(pa):
+    for code in range(0, -6, -1):
+        s = pa.pa_status_string(code)
+        assert s and s != "unknown status"
+    assert pa.pa_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes(pa):
+    assert pa.pa_decode_workspace_bytes(64, 40, 128, 256, 256) == 0       # one partition
+    assert pa.pa_decode_workspace_bytes(64, 40, 128, 2048, 0) > 0         # default 512 -> 4
+    n = pa.pa_decode_workspace_bytes(64, 40, 128, 2048, 512)
+    rows, parts = 64 * 40, 4
+    assert n >= rows * parts * (8 + 4 * 128)
+    assert n % 256 == 0
+    for bad in [(-1, 40, 128, 100, 0), (4, 0, 128, 100, 0), (4, 4, 96, 100, 0),
+                (4, 4, 128, 100, 24), (4, 4, 128, -5, 0)]:
+        with pytest.raises(pa.PAError):
+            pa.pa_decode_workspace_bytes(*bad)
+
+
+# ---------------------------------------------------------------------------
+# host validation (fake device addresses; never run with a GPU visible)
+# ---------------------------------------------------------------------------
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+A = 0x7f0000000000  # 256-byte aligned fake addresses
+OUT, Q, KP, VP, TB, CL, WS = (A + i * 0x100000 for i in range(7))
+
+
+def decode_call(lib, **over):
+    args = dict(out=OUT, q=Q, k_pool=KP, v_pool=VP, block_tables=TB, context_lens=CL,
+                num_seqs=4, num_heads=2, head_dim=64, block_size=16, num_blocks=32,
+                max_blocks_per_seq=4, max_context_len=50, scale=0.125, dtype=1,
+                partition_size=0, workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return lib.pa_decode(*args.values())
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(k_pool=None), -1), (dict(v_pool=None), -1),
+    (dict(block_tables=None), -1), (dict(context_lens=None), -1),
+    (dict(head_dim=96), -3), (dict(block_size=12), -3), (dict(dtype=2), -3),
+    (dict(num_heads=0), -2), (dict(num_blocks=0), -2), (dict(num_seqs=-1), -2),
+    (dict(max_context_len=65), -2), (dict(max_context_len=-1), -2),
+    (dict(partition_size=24), -2), (dict(partition_size=8), -2),
+    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(q=Q + 8), -2), (dict(out=OUT + 2), -2), (dict(k_pool=KP + 4), -2),
+    (dict(block_tables=TB + 2), -2),
+    (dict(partition_size=16), -4),                                   # needs a workspace
+    (dict(partition_size=16, workspace=WS, workspace_bytes=100), -4),
+    (dict(partition_size=16, workspace=WS + 16, workspace_bytes=1 << 20), -2),
+    (dict(num_seqs=70000), -2),
+])
+def test_decode_rejects(pa, over, code):
+    assert decode_call(pa.library(), **over) == code
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+def test_decode_empty_batch_is_ok_without_launch(pa):
+    assert decode_call(pa.library(), num_seqs=0, out=None, q=None) == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+def test_write_and_copy_reject(pa):
+    lib = pa.library()
+    ok = dict(key=Q, value=OUT, k_pool=KP, v_pool=VP, slot_mapping=TB, num_tokens=4, num_heads=2,
+              head_dim=64, block_size=16, num_blocks=32, dtype=0, stream=None)
+
+    def w(**o):
+        a = dict(ok)
+        a.update(o)
+        return lib.pa_write_kv(*a.values())
+
+    assert w(key=None) == -1 and w(slot_mapping=None) == -1
+    assert w(head_dim=32) == -3 and w(block_size=128) == -3 and w(dtype=5) == -3
+    assert w(num_tokens=-1) == -2 and w(key=Q + 8) == -2 and w(slot_mapping=TB + 4) == -2
+    assert w(num_tokens=0, key=None) == 0
+
+    okc = dict(k_pool=KP, v_pool=VP, block_mapping=TB, num_pairs=3, num_heads=2, head_dim=64,
+               block_size=16, num_blocks=32, dtype=0, stream=None)
+
+    def c(**o):
+        a = dict(okc)
+        a.update(o)
+        return lib.pa_copy_blocks(*a.values())
+
+    assert c(block_mapping=None) == -1 and c(v_pool=None) == -1
+    assert c(head_dim=100) == -3 and c(num_pairs=-2) == -2 and c(k_pool=KP + 8) == -2
+    assert c(num_pairs=0, block_mapping=None) == 0

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP kernels behind the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars: bit-exact for pa_write_kv, pa_copy_blocks and every address (pools
+compared as raw bits); pa_decode elementwise within
+|gpu - oracle| <= 2e-3 + 1e-2 |oracle| for fp16 K/V and <= 1e-5 for fp32.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F16_ABS, F16_REL, F32_ABS = 2e-3, 1e-2, 1e-5
+
+
+def announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+
+
+def tbits(t):
+    return bits(t.cpu().numpy())
+
+
+def assert_close(gpu, ref, dtype, where=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    if dtype == W.F16:
+        bound = F16_ABS + F16_REL * np.abs(ref)
+    else:
+        bound = np.full_like(ref, F32_ABS)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{where}: {bad.sum()} elements out of tolerance; first at {tuple(i)}: "
+                             f"gpu={gpu[tuple(i)]!r} oracle={ref[tuple(i)]!r}")
+
+
+def gpu_decode(pa, wl, k, v, device, partition_size=0, ctx=None, tables=None, workspace=None):
+    ctx = wl.context_lens if ctx is None else ctx
+    tables = wl.block_tables if tables is None else tables
+    N, H, D = wl.q.shape
+    q = dev(wl.q, device)
+    out = torch.empty_like(q)
+    maxctx = int(max(int(np.max(ctx)) if len(ctx) else 0, 1))
+    if workspace is None:
+        workspace = pa.new_workspace(N, H, D, maxctx, partition_size, device=device)
+    pa.pa_decode(out, q, k, v, dev(tables, device), dev(ctx, device), float(wl.scale), maxctx,
+                 partition_size=partition_size, workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_decode(oracle, wl, k=None, v=None, **kw):
+    k = wl.k_pool if k is None else k
+    v = wl.v_pool if v is None else v
+    return oracle.decode(wl.q, k, v, wl.block_tables, wl.context_lens, wl.scale, **kw)
+
+
+@functools.lru_cache(maxsize=None)
+def cached(key):
+    name, kw = key[0], dict(key[1:])
+    return W.make(name, **kw)
+
+
+def workload(config, **kw):
+    return cached((config,) + tuple(sorted(kw.items())))
+
+
+# ---------------------------------------------------------------------------
+# the five configurations
+# ---------------------------------------------------------------------------
+
+def step_on_gpu(pa, wl, device):
+    """Pools before the step -> copy-on-write copies -> token writes, on the GPU."""
+    k = dev(wl.k_pool_pre, device)
+    v = dev(wl.v_pool_pre, device)
+    if len(wl.block_mapping):
+        pa.pa_copy_blocks(k, v, dev(wl.block_mapping, device))
+    pa.pa_write_kv(dev(wl.new_key, device), dev(wl.new_value, device), k, v,
+                   dev(wl.slot_mapping, device))
+    torch.cuda.synchronize()
+    return k, v
+
+
+def step_on_oracle(oracle, wl):
+    k, v = wl.k_pool_pre.copy(), wl.v_pool_pre.copy()
+    oracle.copy_blocks(k, v, wl.block_mapping)
+    oracle.write_kv(wl.new_key, wl.new_value, k, v, wl.slot_mapping)
+    return k, v
+
+
+@pytest.mark.parametrize("config,kw", [
+    (1, {}),
+    (2, {}),
+    (3, {"block_size": 16}),
+    (4, {}),
+], ids=["cfg1-tiny-fp32", "cfg2-opt13b", "cfg3-short", "cfg4-cow"])
+def test_step_then_decode(pa, oracle_lib, device, config, kw):
+    wl = workload(config, **kw)
+    announce(f"{wl.name}: N={wl.num_seqs} H={wl.num_heads} D={wl.head_dim} B={wl.block_size} "
+             f"NB={wl.num_blocks} pairs={len(wl.block_mapping)} tokens={len(wl.slot_mapping)}")
+    k, v = step_on_gpu(pa, wl, device)
+    ok, ov = step_on_oracle(oracle_lib, wl)
+    assert np.array_equal(tbits(k), bits(ok)), "K pool after copy+write differs"
+    assert np.array_equal(tbits(v), bits(ov)), "V pool after copy+write differs"
+    announce(f"{wl.name}: pa_decode")
+    got = gpu_decode(pa, wl, k, v, device)
+    ref = oracle_decode(oracle_lib, wl, ok, ov)
+    assert_close(got, ref, wl.dtype, wl.name)
+    one = np.flatnonzero(wl.context_lens == 1)
+    for b in one:  # a single token returns its V row exactly
+        assert np.array_equal(bits(got[b]), bits(wl.logical_v[b][0]))
+
+
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+def test_block_size_sweep(pa, oracle_lib, device, B):
+    """Config 3's sweep: same sequences and logical K/V for B = 8..64; every B
+    matches the oracle and the GPU output is bit-identical across B (the
+    kernel's summation order depends on logical positions only)."""
+    wl = workload(3, block_size=B)
+    announce(f"{wl.name}: N={wl.num_seqs} B={B}")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
+    assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
+    base = workload(3, block_size=16)
+    if B != 16:
+        ref = gpu_decode(pa, base, dev(base.k_pool, device), dev(base.v_pool, device), device)
+        assert np.array_equal(bits(got), bits(ref))
+
+
+def test_config5_long_context_sampled(pa, oracle_lib, device):
+    """OPT-175B layer shape, all 96 heads, contexts 4K-16K: the full batch on the
+    GPU (device-filled pools), checked against the oracle on sampled rows with
+    the real block table."""
+    wl = W.config5(host=False)
+    announce(f"{wl.name}: N={wl.num_seqs} H={wl.num_heads} NB={wl.num_blocks} filling pools")
+    k, v = W.device_pools(wl, device)
+    announce(f"{wl.name}: pa_decode default partition")
+    got = gpu_decode(pa, wl, k, v, device)
+    rng = np.random.default_rng(55)
+    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, wl.num_seqs, 8),
+                                             rng.integers(0, wl.num_heads, 8))]
+    rows.append((int(np.argmax(wl.context_lens)), 0))
+    for b, h in rows:
+        n = int(wl.context_lens[b])
+        blocks = wl.block_tables[b, :-(-n // 16)].astype(np.int64)
+        kh = np.full((wl.num_blocks, 1, 16, 128), np.nan, np.float16)
+        vh = kh.copy()
+        idx = torch.as_tensor(blocks, device=device)
+        kh[blocks] = k[idx, h:h + 1].cpu().numpy()
+        vh[blocks] = v[idx, h:h + 1].cpu().numpy()
+        ref = oracle_lib.decode(wl.q[b:b + 1, h:h + 1], kh, vh, wl.block_tables[b:b + 1],
+                                wl.context_lens[b:b + 1], wl.scale)
+        assert_close(got[b:b + 1, h:h + 1], ref, wl.dtype, f"{wl.name} row ({b},{h}) ctx={n}")
+    announce(f"{wl.name}: partition 1024 agrees")
+    got2 = gpu_decode(pa, wl, k, v, device, partition_size=1024)
+    assert np.abs(got2.astype(np.float64) - got.astype(np.float64)).max() <= 2e-3
+    del k, v
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# partitions, invariances, edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("part", [16, 48, 128, 256, 512, 1024, 4096])
+def test_partition_sizes(pa, oracle_lib, device, part):
+    wl = workload(2, num_seqs=24, num_heads=8)
+    announce(f"{wl.name} small: partition {part}")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
+                     partition_size=part)
+    assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, f"partition {part}")
+
+
+def test_placement_invariance_bit_identical(pa, device):
+    wl = workload(2, num_seqs=24, num_heads=8)
+    ref = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
+    for s in range(2):
+        r = W.relayout(wl, s)
+        announce(f"relayout {s}")
+        got = gpu_decode(pa, r, dev(r.k_pool, device), dev(r.v_pool, device), device)
+        assert np.array_equal(bits(got), bits(ref))
+
+
+def test_shared_prefix_bit_identical_to_private_copies(pa, device):
+    wl = workload(4, num_prompts=6, samples=6, num_heads=4)
+    ref = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
+    r = W.relayout(wl, 9)
+    got = gpu_decode(pa, r, dev(r.k_pool, device), dev(r.v_pool, device), device)
+    assert np.array_equal(bits(got), bits(ref))
+
+
+EDGE_CTX = [1, 2, 3, 4, 5, 15, 16, 17, 31, 33, 63, 64, 65, 255, 256, 257, 511, 777]
+
+
+@pytest.mark.parametrize("dtype,D,B", [(W.F16, 128, 16), (W.F16, 128, 8), (W.F16, 64, 64),
+                                       (W.F16, 64, 8), (W.F32, 64, 16), (W.F32, 128, 32),
+                                       (W.F32, 128, 8), (W.F16, 128, 32)])
+@pytest.mark.parametrize("part", [0, 64])
+def test_edge_contexts(pa, oracle_lib, device, dtype, D, B, part):
+    H = 3
+    wl = W._simple(f"edge-{dtype}-D{D}-B{B}", 77, dtype, H, D, B, EDGE_CTX)
+    announce(f"{wl.name} part={part}")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
+                     partition_size=part)
+    ref = oracle_decode(oracle_lib, wl)
+    assert_close(got, ref, dtype, wl.name)
+    assert np.array_equal(bits(got[0]), bits(wl.logical_v[0][0]))  # ctx 1 -> V exactly
+    assert np.isfinite(got).all()                                     # NaN in unused slots never leaks
+
+
+def test_zero_context_and_max_context(pa, oracle_lib, device):
+    B, MB = 16, 6
+    wl = W._simple("zero-max", 5, W.F16, 2, 128, B, [5, MB * B, 1, MB * B], MB=MB)
+    ctx = wl.context_lens.copy()
+    ctx[2] = 0
+    announce("zero and max contexts")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device, ctx=ctx,
+                     partition_size=32)
+    ref = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, ctx, wl.scale)
+    assert np.array_equal(got[2], np.zeros_like(got[2]))
+    assert_close(got, ref, W.F16, "zero/max")
+
+
+def test_out_of_range_table_entry_poisons_only_its_row(pa, oracle_lib, device):
+    wl = workload(2, num_seqs=24, num_heads=8)
+    tables = wl.block_tables.copy()
+    victim = int(np.argmax(wl.context_lens))
+    tables[victim, 1] = wl.num_blocks + 1000  # outside the pool: the kernel must not read it
+    announce("out-of-range table entry")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device, tables=tables,
+                     partition_size=64)
+    assert np.isnan(got[victim].astype(np.float32)).all()
+    others = [b for b in range(wl.num_seqs) if b != victim]
+    ref = oracle_decode(oracle_lib, wl)
+    assert_close(got[others], ref[others], wl.dtype, "other rows")
+
+
+def test_workspace_contents_ignored_and_reused(pa, oracle_lib, device):
+    """Workspace contents on entry do not matter: one buffer, filled with NaN
+    bit patterns between calls, serves calls of different batch shapes."""
+    big = workload(2, num_seqs=24, num_heads=8)
+    small = workload(3, block_size=16, num_seqs=12, num_heads=4)
+    n = pa.pa_decode_workspace_bytes(big.num_seqs, big.num_heads, 128, big.max_context_len, 32)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    kb, vb = dev(big.k_pool, device), dev(big.v_pool, device)
+    ks, vs = dev(small.k_pool, device), dev(small.v_pool, device)
+    ref_big, ref_small = oracle_decode(oracle_lib, big), oracle_decode(oracle_lib, small)
+    announce("workspace contents ignored")
+    for fill in (0xFF, 0x7F, 0x00):
+        ws.fill_(fill)
+        a = gpu_decode(pa, big, kb, vb, device, partition_size=32, workspace=ws)
+        assert_close(a, ref_big, big.dtype, f"big after fill {fill:#x}")
+        b = gpu_decode(pa, small, ks, vs, device, partition_size=32, workspace=ws)
+        assert_close(b, ref_small, small.dtype, f"small after fill {fill:#x}")
+
+
+@pytest.mark.parametrize("dtype,D,B", [(W.F16, 128, 16), (W.F32, 64, 8), (W.F16, 64, 64),
+                                       (W.F32, 128, 32)])
+def test_write_and_copy_random_bits(pa, oracle_lib, device, dtype, D, B):
+    """Pools and rows of random bit patterns (NaN payloads, -0, infinities):
+    writes (with padding slots) and copies move bits exactly."""
+    rng = np.random.default_rng(D + B)
+    H, NB, T = 3, 40, 25
+    u = np.uint16 if dtype == W.F16 else np.uint32
+    npd = W.NP_DTYPES[dtype]
+    info = np.iinfo(u)
+    rb = lambda shape: rng.integers(0, info.max, size=shape, dtype=u, endpoint=True).view(npd)
+    k0, v0 = rb((NB, H, B, D)), rb((NB, H, B, D))
+    key, val = rb((T, H, D)), rb((T, H, D))
+    slots = rng.choice(NB * B, size=T, replace=False).astype(np.int64)
+    slots[::7] = -1                                   # padding tokens are skipped
+    pairs = np.array([[3, 10], [3, 11], [5, 12], [39, 0]], np.int64)
+    announce(f"write/copy random bits {dtype} D{D} B{B}")
+    k, v = dev(k0, device), dev(v0, device)
+    pa.pa_copy_blocks(k, v, dev(pairs, device))
+    pa.pa_write_kv(dev(key, device), dev(val, device), k, v, dev(slots, device))
+    torch.cuda.synchronize()
+    ok, ov = k0.copy(), v0.copy()
+    oracle_lib.copy_blocks(ok, ov, pairs)
+    oracle_lib.write_kv(key, val, ok, ov, slots)
+    assert np.array_equal(tbits(k), bits(ok))
+    assert np.array_equal(tbits(v), bits(ov))
+
+
+def test_write_skips_slots_outside_pool(pa, oracle_lib, device):
+    H, D, B, NB = 2, 128, 16, 8
+    rng = np.random.default_rng(4)
+    k0 = rng.standard_normal((NB, H, B, D)).astype(np.float16)
+    key = rng.standard_normal((3, H, D)).astype(np.float16)
+    slots = np.array([5, NB * B, 7], np.int64)        # the middle one is outside the pool
+    k, v = dev(k0, device), dev(k0, device)
+    announce("write with an out-of-pool slot")
+    pa.pa_write_kv(dev(key, device), dev(key, device), k, v, dev(slots, device))
+    torch.cuda.synchronize()
+    ok, ov = k0.copy(), k0.copy()
+    oracle_lib.write_kv(key[[0, 2]], key[[0, 2]], ok, ov, slots[[0, 2]])
+    assert np.array_equal(tbits(k), bits(ok)) and np.array_equal(tbits(v), bits(ov))
+
+
+def test_nondefault_stream(pa, oracle_lib, device):
+    wl = workload(1)
+    s = torch.cuda.Stream()
+    k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
+    q = dev(wl.q, device)
+    out = torch.empty_like(q)
+    tabs, ctx = dev(wl.block_tables, device), dev(wl.context_lens, device)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        pa.pa_decode(out, q, k, v, tabs, ctx, float(wl.scale), wl.max_context_len)
+    s.synchronize()
+    assert_close(out.cpu().numpy(), oracle_decode(oracle_lib, wl), wl.dtype, "stream")
