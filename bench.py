@@ -186,7 +186,7 @@ def main():
             "context_lens": "lognormal median 300 sigma 0.9 clipped [1,2048]",
             "sum_context": int(wl.context_lens.sum()), "max_context": maxctx,
             "num_blocks": wl.num_blocks, "layer_pools_rotated": L,
-            "partition_size": args.partition or pa.PA_DEFAULT_PARTITION,
+            "partition_size": args.partition or pa.default_partition(maxctx),
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),

@@ -64,13 +64,17 @@ extern "C" {
 
 /* Supported sizes: head_dim in {64, 128}; block_size in {8, 16, 32, 64}. */
 
-/* Partition length used when pa_decode is given partition_size == 0. */
-#define PA_DEFAULT_PARTITION 512
+/* Partition length used when pa_decode is given partition_size == 0:
+ * PA_DEFAULT_PARTITION tokens, or PA_LONG_PARTITION when max_context_len
+ * exceeds PA_LONG_CONTEXT. */
+#define PA_DEFAULT_PARTITION 1024
+#define PA_LONG_PARTITION 4096
+#define PA_LONG_CONTEXT 8192
 
 /*
  * Bytes of workspace pa_decode needs for this batch shape:
  * ceil(max_context_len / P) partitions per (sequence, head), where P is the
- * partition length (partition_size, or PA_DEFAULT_PARTITION when 0).  Returns
+ * partition length (partition_size, or the default above when 0).  Returns
  * 0 when every context fits in one partition (no workspace needed) and
  * (size_t)-1 for invalid arguments.
  */
@@ -103,7 +107,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
  *                  the host never reads device data
  *   scale          multiplier of the dot products (usually 1/sqrt(head_dim))
  *   partition_size tokens per context partition, a multiple of 16 in
- *                  [16, 65536], or 0 for PA_DEFAULT_PARTITION.  Contexts longer
+ *                  [16, 65536], or 0 for the default above.  Contexts longer
  *                  than one partition are split across workgroups and merged
  *                  exactly (max/sum rescaling).
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)

@@ -25,7 +25,14 @@ LIBRARY = os.path.join(HERE, "libpa.so")
 PA_OK = 0
 PA_F16 = 0
 PA_F32 = 1
-PA_DEFAULT_PARTITION = 512
+PA_DEFAULT_PARTITION = 1024
+PA_LONG_PARTITION = 4096
+PA_LONG_CONTEXT = 8192
+
+
+def default_partition(max_context_len: int) -> int:
+    """The partition length pa_decode uses when given partition_size 0."""
+    return PA_LONG_PARTITION if max_context_len > PA_LONG_CONTEXT else PA_DEFAULT_PARTITION
 
 # Every symbol include/pa.h declares.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_write_kv", "pa_copy_blocks",

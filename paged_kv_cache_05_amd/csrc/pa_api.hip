@@ -31,8 +31,12 @@ int check_pool(int num_heads, int head_dim, int block_size, int num_blocks, int 
   return PA_OK;
 }
 
-int effective_partition(int partition_size) {
-  return partition_size == 0 ? PA_DEFAULT_PARTITION : partition_size;
+// partition_size 0: PA_DEFAULT_PARTITION, or PA_LONG_PARTITION once the
+// longest context exceeds PA_LONG_CONTEXT (fewer, longer partitions amortise
+// each workgroup's epilogue when every row is long).
+int effective_partition(int partition_size, int max_context_len) {
+  if (partition_size != 0) return partition_size;
+  return max_context_len > PA_LONG_CONTEXT ? PA_LONG_PARTITION : PA_DEFAULT_PARTITION;
 }
 
 bool valid_partition(int part) { return part >= 16 && part <= kMaxPartition && part % 16 == 0; }
@@ -61,7 +65,7 @@ const char *pa_status_string(int status) {
 
 size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                  int partition_size) {
-  const int part = effective_partition(partition_size);
+  const int part = effective_partition(partition_size, max_context_len);
   if (num_seqs < 0 || num_heads <= 0 || !supported_head_dim(head_dim) || max_context_len < 0 ||
       !valid_partition(part))
     return (size_t)-1;
@@ -77,7 +81,7 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
               int partition_size, void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
-  const int part = effective_partition(partition_size);
+  const int part = effective_partition(partition_size, max_context_len);
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
       !valid_partition(part) || !isfinite(scale) || num_seqs > kGridYZ || num_heads > kGridYZ ||

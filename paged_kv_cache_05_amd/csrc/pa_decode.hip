@@ -91,6 +91,19 @@ __device__ __forceinline__ Chunk load_chunk(const char *p) {
   return c;
 }
 
+// K/V rows are read exactly once per call: non-temporal loads keep them from
+// displacing reusable lines (block tables, q) in the caches.
+__device__ __forceinline__ Chunk load_stream(const char *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  Chunk c;
+  c.w[0] = x.x;
+  c.w[1] = x.y;
+  c.w[2] = x.z;
+  c.w[3] = x.w;
+  return c;
+}
+
 __device__ __forceinline__ float dot_chunk(const Chunk &q, const Chunk &k, float acc, _Float16) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -147,12 +160,13 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
   __shared__ float s_l[kStates];
   __shared__ float s_o[kStates][D];
 
-  // Partition index is the slowest grid dimension: every partition-0
-  // workgroup (always busy) is dispatched before those of later
-  // partitions, many of which find their sequence too short and exit.
+  // Partition index is the slowest grid dimension, counted down: the last
+  // partitions, which exist only for the longest sequences, are dispatched
+  // first and partition 0 (every row, including the short ones) last, so
+  // the work that trails the launch is the smallest.
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int part = blockIdx.z;
+  const int part = p.num_partitions - 1 - (int)blockIdx.z;
   const int H = p.num_heads;
   const size_t row = (size_t)b * H + h;
 
@@ -213,8 +227,8 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
         const size_t boff = (size_t)(ok ? phys : 0) * block_bytes + (size_t)off * D * sizeof(T);
 #pragma unroll
         for (int k = 0; k < G::kChunksPerLane; ++k) {
-          tile.k[g][k] = load_chunk(kbase + boff + k * kLPT * 16);
-          tile.v[g][k] = load_chunk(vbase + boff + k * kLPT * 16);
+          tile.k[g][k] = load_stream(kbase + boff + k * kLPT * 16);
+          tile.v[g][k] = load_stream(vbase + boff + k * kLPT * 16);
         }
       } else {
 #pragma unroll

@@ -39,6 +39,8 @@ def test_header_constants_match_binding(pa):
     assert int(consts["PA_OK"]) == pa.PA_OK
     assert int(consts["PA_F16"]) == pa.PA_F16 and int(consts["PA_F32"]) == pa.PA_F32
     assert int(consts["PA_DEFAULT_PARTITION"]) == pa.PA_DEFAULT_PARTITION
+    assert int(consts["PA_LONG_PARTITION"]) == pa.PA_LONG_PARTITION
+    assert int(consts["PA_LONG_CONTEXT"]) == pa.PA_LONG_CONTEXT
 
 
 def test_status_strings(pa):
@@ -50,7 +52,11 @@ def test_status_strings(pa):
 
 def test_workspace_bytes(pa):
     assert pa.pa_decode_workspace_bytes(64, 40, 128, 256, 256) == 0       # one partition
-    assert pa.pa_decode_workspace_bytes(64, 40, 128, 2048, 0) > 0         # default 512 -> 4
+    assert pa.pa_decode_workspace_bytes(64, 40, 128, 1024, 0) == 0        # default 1024
+    assert pa.pa_decode_workspace_bytes(64, 40, 128, 2048, 0) > 0         # default 1024 -> 2
+    # past PA_LONG_CONTEXT the default partition is PA_LONG_PARTITION
+    assert pa.pa_decode_workspace_bytes(32, 96, 128, 16384, 0) == \
+        pa.pa_decode_workspace_bytes(32, 96, 128, 16384, 4096)
     n = pa.pa_decode_workspace_bytes(64, 40, 128, 2048, 512)
     rows, parts = 64 * 40, 4
     assert n >= rows * parts * (8 + 4 * 128)
