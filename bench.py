@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: HBM GB/s (% of peak), decode steps/s at OPT-13B shape"
 PEAK_HBM_GBS = 8000.0
-COUNTER_FILE = os.path.join(ROOT, "profiles", "pa_decode_opt13b_hbm_counters.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "pa_decode_opt13b_hbm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_05_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_kernels.h")]
 
@@ -46,16 +46,37 @@ def kernel_digest():
 
 
 def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    if they were taken on the kernel source as it is now."""
+    """HBM bytes per decode call from the committed rocprofv3 counter runs
+    (``key: value`` lines), if they were taken on the kernel source as it is
+    now; otherwise None."""
     try:
         with open(COUNTER_FILE) as f:
-            c = json.load(f)
-    except (OSError, ValueError):
+            c = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
         return None
+    c = {k.strip(): v.strip() for k, v in c.items()}
     if c.get("kernel_digest") != kernel_digest():
         return None
-    return c.get("hbm_bytes_per_launch")
+    try:
+        return int(c["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """One plain device copy of known size (1 GiB read, 1 GiB written), for
+    scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 28  # fp32 elements: 1 GiB
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch.mul fp32 copy", "read_bytes": 4 * n,
+                      "write_bytes": 4 * n}), flush=True)
+    return 0
 
 
 def main():
@@ -67,12 +88,15 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run one 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+                    help="only run one 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus "
               f"{args.gpus}", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy:
+        return calibrate_copy()
 
     import torch
 
@@ -94,13 +118,6 @@ def main():
     ws = pa.new_workspace(N, H, D, maxctx, args.partition, device=device)
     scale = float(wl.scale)
     stream = torch.cuda.current_stream()
-
-    if args.calibrate_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=device)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
 
     def step(i, ev=None):
         k, v = pools[i % L]
@@ -200,7 +217,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "pa::decode_kernel<f16, 128, 16, 8>",
+            "kernel": "pa_decode call: decode_kernel<f16,128,16,8> + merge_kernel<f16,128>",
         },
         "cpu_baseline": cpu,
         "parity_layer0_vs_oracle": parity,
