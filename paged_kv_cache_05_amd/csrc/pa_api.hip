@@ -110,8 +110,7 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   if (p.num_partitions > 1) {
     const pa::WorkspaceLayout w =
         pa::decode_workspace_layout(num_seqs, num_heads, head_dim, p.num_partitions);
-    if (!workspace) return PA_ERR_WORKSPACE;
-    if (workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return PA_ERR_SHAPE;
     char *base = static_cast<char *>(workspace);
     p.part_ml = reinterpret_cast<float2 *>(base + w.ml_off);

@@ -150,37 +150,32 @@ struct RowState {
   float acc[kAcc];
 };
 
+// LDS of one workgroup: the W * kTokensPerGroup row states it merges.
+template <typename T, int D, int W>
+struct ItemShared {
+  static constexpr int kStates = W * Geometry<T, D>::kTokensPerGroup;
+  float m[kStates];
+  float l[kStates];
+  float o[kStates][D];
+};
+
+// One work item: sequence b, head h, context partition `part` (tokens
+// [part * P, min(ctx, (part + 1) * P)), non-empty), ctx already clamped.
+// Called by every thread of the workgroup (it synchronises inside).  Writes
+// the output row when the row has a single partition, else this partition's
+// (max, sum, unnormalised output) for the merge pass.
 template <typename T, int D, int B, int W>
-__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
+__device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T, D, W> &sh,
+                                             int b, int h, int part, int ctx) {
   using G = Geometry<T, D>;
-  constexpr int kStates = W * G::kTokensPerGroup;
+  constexpr int kStates = ItemShared<T, D, W>::kStates;
   constexpr int kLPT = G::kLanesPerToken;
   constexpr int kTPG = G::kTokensPerGroup;
-  __shared__ float s_m[kStates];
-  __shared__ float s_l[kStates];
-  __shared__ float s_o[kStates][D];
-
-  // Partition index is the slowest grid dimension, counted down: the last
-  // partitions, which exist only for the longest sequences, are dispatched
-  // first and partition 0 (every row, including the short ones) last, so
-  // the work that trails the launch is the smallest.
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int part = p.num_partitions - 1 - (int)blockIdx.z;
   const int H = p.num_heads;
   const size_t row = (size_t)b * H + h;
-
-  int ctx = p.context_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
   T *out_row = reinterpret_cast<T *>(p.out) + row * D;
-  if (ctx == 0) {
-    if (part == 0)
-      for (int d = threadIdx.x; d < D; d += 64 * W) out_row[d] = T(0);
-    return;
-  }
   const int P = p.partition_size;
   const int tok0 = part * P;
-  if (tok0 >= ctx) return;
   const int tok_end = min(ctx, tok0 + P);
   const int n_parts = (ctx + P - 1) / P;
 
@@ -332,25 +327,25 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
   {
     const int sidx = wave * kTPG + trow;
     if (col == 0) {
-      s_m[sidx] = st.m;
-      s_l[sidx] = st.l;
+      sh.m[sidx] = st.m;
+      sh.l[sidx] = st.l;
     }
 #pragma unroll
     for (int k = 0; k < G::kChunksPerLane; ++k)
 #pragma unroll
       for (int i = 0; i < G::kPerChunk; ++i)
-        s_o[sidx][(col + k * kLPT) * G::kPerChunk + i] = st.acc[k * G::kPerChunk + i];
+        sh.o[sidx][(col + k * kLPT) * G::kPerChunk + i] = st.acc[k * G::kPerChunk + i];
   }
   __syncthreads();
 
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kStates; ++s) M = fmaxf(M, s_m[s]);
+  for (int s = 0; s < kStates; ++s) M = fmaxf(M, sh.m[s]);
   float lsum = 0.f;
 #pragma unroll
   for (int s = 0; s < kStates; ++s) {
-    const float ms = s_m[s];
-    lsum += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_l[s];
+    const float ms = sh.m[s];
+    lsum += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * sh.l[s];
   }
 
   if (n_parts == 1) {
@@ -358,8 +353,8 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
       float o = 0.f;
 #pragma unroll
       for (int s = 0; s < kStates; ++s) {
-        const float ms = s_m[s];
-        o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_o[s][d];
+        const float ms = sh.m[s];
+        o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * sh.o[s][d];
       }
       out_row[d] = T(o / lsum);
     }
@@ -373,12 +368,37 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
     float o = 0.f;
 #pragma unroll
     for (int s = 0; s < kStates; ++s) {
-      const float ms = s_m[s];
-      o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * s_o[s][d];
+      const float ms = sh.m[s];
+      o += (ms == -INFINITY ? 0.f : fast_exp2(ms - M)) * sh.o[s][d];
     }
     po[d] = o;
   }
   if (threadIdx.x == 0) p.part_ml[row * NP + part] = make_float2(M, lsum);
+}
+
+// One workgroup per (head, sequence, partition); the hardware dispatcher
+// hands slots to workgroups as earlier ones finish.
+template <typename T, int D, int B, int W>
+__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
+  __shared__ ItemShared<T, D, W> sh;
+  // Partition index is the slowest grid dimension, counted down: the last
+  // partitions, which exist only for the longest sequences, are dispatched
+  // first and partition 0 (every row, including the short ones) last, so
+  // the work that trails the launch is the smallest.
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = p.num_partitions - 1 - (int)blockIdx.z;
+  int ctx = p.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
+  if (ctx == 0) {
+    if (part == 0) {
+      T *out_row = reinterpret_cast<T *>(p.out) + ((size_t)b * p.num_heads + h) * D;
+      for (int d = threadIdx.x; d < D; d += 64 * W) out_row[d] = T(0);
+    }
+    return;
+  }
+  if (part * p.partition_size >= ctx) return;
+  process_item<T, D, B, W>(p, sh, b, h, part, ctx);
 }
 
 // Second pass, rows with several partitions only: out = sum_p w_p o_p /

@@ -270,6 +270,16 @@ def test_workspace_contents_ignored_and_reused(pa, oracle_lib, device):
         assert_close(b, ref_small, small.dtype, f"small after fill {fill:#x}")
 
 
+def test_large_batch(pa, oracle_lib, device):
+    """A batch of 1100 short sequences."""
+    ctx = np.random.default_rng(8).integers(1, 90, size=1100)
+    wl = W._simple("many-seqs", 8, W.F16, 2, 64, 16, ctx)
+    announce(f"large batch: N={wl.num_seqs}")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
+                     partition_size=32)
+    assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, "large batch")
+
+
 @pytest.mark.parametrize("dtype,D,B", [(W.F16, 128, 16), (W.F32, 64, 8), (W.F16, 64, 64),
                                        (W.F32, 128, 32)])
 def test_write_and_copy_random_bits(pa, oracle_lib, device, dtype, D, B):
@@ -320,8 +330,10 @@ def test_nondefault_stream(pa, oracle_lib, device):
     q = dev(wl.q, device)
     out = torch.empty_like(q)
     tabs, ctx = dev(wl.block_tables, device), dev(wl.context_lens, device)
+    ws = pa.new_workspace(wl.num_seqs, wl.num_heads, wl.head_dim, wl.max_context_len,
+                          device=device)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        pa.pa_decode(out, q, k, v, tabs, ctx, float(wl.scale), wl.max_context_len)
+        pa.pa_decode(out, q, k, v, tabs, ctx, float(wl.scale), wl.max_context_len, workspace=ws)
     s.synchronize()
     assert_close(out.cpu().numpy(), oracle_decode(oracle_lib, wl), wl.dtype, "stream")
