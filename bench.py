@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="layer pools to rotate over")
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-lengths", action="store_true",
+                    help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -117,6 +119,9 @@ def main():
     maxctx = wl.max_context_len
     ws = pa.new_workspace(N, H, D, maxctx, args.partition, device=device)
     scale = float(wl.scale)
+    # The step's scheduler knows every context length on the host; passing
+    # them lets pa_decode launch only non-empty work items, largest first.
+    host_ctx = None if args.no_host_lengths else wl.context_lens
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -125,7 +130,8 @@ def main():
         pa.pa_write_kv(new_k, new_v, k, v, slots)
         if ev is not None:
             ev[0].record(stream)
-        pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws)
+        pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws,
+                     host_context_lens=host_ctx)
         if ev is not None:
             ev[1].record(stream)
 
@@ -158,7 +164,8 @@ def main():
     # Output of layer 0 for the parity sample and the CPU baseline.
     k0, v0 = pools[0]
     pa.pa_write_kv(new_k, new_v, k0, v0, slots)
-    pa.pa_decode(out, q, k0, v0, tables, ctx, scale, maxctx, args.partition, ws)
+    pa.pa_decode(out, q, k0, v0, tables, ctx, scale, maxctx, args.partition, ws,
+                 host_context_lens=host_ctx)
     torch.cuda.synchronize()
     gpu_out = out.cpu().numpy().astype(np.float64)
     if not np.isfinite(gpu_out).all():
@@ -204,6 +211,7 @@ def main():
             "sum_context": int(wl.context_lens.sum()), "max_context": maxctx,
             "num_blocks": wl.num_blocks, "layer_pools_rotated": L,
             "partition_size": args.partition or pa.default_partition(maxctx),
+            "host_planned_launch": host_ctx is not None,
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),

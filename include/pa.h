@@ -110,6 +110,18 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
  *                  [16, 65536], or 0 for the default above.  Contexts longer
  *                  than one partition are split across workgroups and merged
  *                  exactly (max/sum rescaling).
+ *   host_context_lens optional HOST copy of context_lens (NULL: none).  The
+ *                  step's scheduler has the lengths on the host anyway
+ *                  ([wywy] WHERE: the central KV cache manager tracks each
+ *                  sequence and sends the per-step inputs to the workers).
+ *                  With it, the library launches exactly the non-empty
+ *                  (sequence, partition) work items, largest first, and
+ *                  merges only the sequences that span several partitions
+ *                  (up to 960 items; beyond that, and without it, one
+ *                  workgroup per (head, sequence, partition) is launched
+ *                  and empty ones leave at once).  Each entry must be at
+ *                  least the device value it copies (equal for the best
+ *                  schedule); the device values still decide every result.
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
  *                  bytes (256-byte aligned), or NULL when that is 0: the
  *                  per-partition partial results (max, sum, unnormalised
@@ -117,15 +129,16 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
  *                  entry are ignored; concurrent calls must not share one
  *                  workspace.
  *
- * Launches one kernel, plus a small merge kernel when max_context_len
- * exceeds one partition.  Workgroups own (head, sequence, partition); rows
- * that fit one partition are finished by the first kernel.
+ * Launches one kernel, plus a small merge kernel when some row spans several
+ * partitions.  Workgroups own (head, sequence, partition); rows that fit one
+ * partition are finished by the first kernel.
  */
 int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
               const int32_t *block_tables, const int32_t *context_lens,
               int num_seqs, int num_heads, int head_dim, int block_size,
               int num_blocks, int max_blocks_per_seq, int max_context_len,
               float scale, int dtype, int partition_size,
+              const int32_t *host_context_lens,
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*

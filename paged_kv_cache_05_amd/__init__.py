@@ -57,7 +57,7 @@ def library() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIBRARY)
     vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                              f32, i32, i32, vp, sz, vp]
+                              f32, i32, i32, vp, vp, sz, vp]
     lib.pa_decode.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = sz
@@ -126,14 +126,22 @@ def new_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size
 
 
 def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None):
+              partition_size=0, workspace=None, stream=None, host_context_lens=None):
     """out[N][H][D] = paged decode attention of q[N][H][D] over the pools.
 
     k_pool/v_pool: [num_blocks][H][block_size][D]; block_tables int32
     [N][max_blocks_per_seq]; context_lens int32 [N]; max_context_len: host
-    int >= every context length; workspace: from :func:`new_workspace`.
+    int >= every context length; workspace: from :func:`new_workspace`;
+    host_context_lens: optional host copy of context_lens (numpy int32 or a
+    sequence of ints), used only to plan the launch.
     """
+    import numpy as np
     import torch
+    host = None
+    if host_context_lens is not None:
+        host = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+        if host.shape != (q.shape[0],):
+            raise PAError("host_context_lens must have one entry per sequence")
     N, H, D = q.shape
     NB, H2, B, D2 = k_pool.shape
     if (H2, D2) != (H, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
@@ -150,7 +158,8 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         N, H, D, B, NB, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
-        int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+        int(partition_size), None if host is None else host.ctypes.data, ws_ptr, ws_bytes,
+        _stream(stream))
     _check(rc, "pa_decode")
     return out
 

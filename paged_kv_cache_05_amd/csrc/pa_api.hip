@@ -4,6 +4,8 @@
 // device memory.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/pa.h"
 #include "pa_kernels.h"
 
@@ -47,6 +49,80 @@ int num_partitions(int max_context_len, int part) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+int clamp_ctx(int32_t c, int max_context_len) {
+  return c < 0 ? 0 : (c > max_context_len ? max_context_len : c);
+}
+
+// Work list from host-side context lengths: every (sequence, partition)
+// with at least one token (one entry for an empty sequence, whose row is
+// zeroed); and the sequences that span several partitions.  Items longer
+// than twice the mean go first, longest first, so that no long item starts
+// late; the rest keep (sequence, partition) order, which keeps neighbouring
+// sequences (for instance parallel samples sharing prompt blocks) close in
+// time and mixes sizes so that concurrently running workgroups stay busy.
+// False when either list would exceed the kernel-argument capacity.
+bool plan_work(const int32_t *host_ctx, int num_seqs, int max_context_len, int part,
+               pa::WorkList *items, pa::WorkList *merge_rows) {
+  int total = 0;
+  long long tokens = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int c = clamp_ctx(host_ctx[b], max_context_len);
+    total += c == 0 ? 1 : (c + part - 1) / part;
+    tokens += c;
+    if (total > pa::kMaxListed) return false;
+  }
+  struct Entry {
+    int tokens;
+    uint32_t item;
+  };
+  Entry e[pa::kMaxListed];
+  int n = 0;
+  merge_rows->count = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int c = clamp_ctx(host_ctx[b], max_context_len);
+    const int np = c == 0 ? 1 : (c + part - 1) / part;
+    for (int q = 0; q < np; ++q)
+      e[n++] = Entry{std::min(part, c - q * part), ((uint32_t)b << 16) | (uint32_t)q};
+    if (np > 1) merge_rows->item[merge_rows->count++] = (uint32_t)b;
+  }
+  const long long long_item = 2 * tokens / n;  // twice the mean item length
+  Entry *mid = std::stable_partition(
+      e, e + n, [long_item](const Entry &x) { return (long long)x.tokens > long_item; });
+  std::stable_sort(e, mid, [](const Entry &x, const Entry &y) { return x.tokens > y.tokens; });
+  items->count = n;
+  for (int i = 0; i < n; ++i) items->item[i] = e[i].item;
+  return true;
+}
+
+// Partition length when the caller leaves it to the library and passes
+// host-side lengths: start from PA_LONG_PARTITION and halve while the batch
+// offers fewer than kPlanTargetItems workgroups' worth of (head, sequence,
+// partition) items, down to kPlanMinPartition, never below what the
+// workspace can hold.
+constexpr long long kPlanTargetItems = 2048;
+constexpr int kPlanMinPartition = 256;
+
+int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int head_dim,
+                   int max_context_len, size_t workspace_bytes, bool have_workspace) {
+  int part = PA_LONG_PARTITION;
+  for (;;) {
+    long long items = 0;
+    for (int b = 0; b < num_seqs; ++b) {
+      const int c = clamp_ctx(host_ctx[b], max_context_len);
+      items += (long long)num_heads * (c == 0 ? 1 : (c + part - 1) / part);
+    }
+    const int next = part / 2;
+    if (items >= kPlanTargetItems || next < kPlanMinPartition) break;
+    const int np = num_partitions(max_context_len, next);
+    if (np > 1 && (!have_workspace ||
+                   pa::decode_workspace_layout(num_seqs, num_heads, head_dim, np).total >
+                       workspace_bytes))
+      break;
+    part = next;
+  }
+  return part;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,10 +154,11 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
               const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
               int num_heads, int head_dim, int block_size, int num_blocks,
               int max_blocks_per_seq, int max_context_len, float scale, int dtype,
-              int partition_size, void *workspace, size_t workspace_bytes, void *stream) {
+              int partition_size, const int32_t *host_context_lens, void *workspace,
+              size_t workspace_bytes, void *stream) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
-  const int part = effective_partition(partition_size, max_context_len);
+  int part = effective_partition(partition_size, max_context_len);
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
       !valid_partition(part) || !isfinite(scale) || num_seqs > kGridYZ || num_heads > kGridYZ ||
@@ -92,6 +169,9 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return PA_ERR_SHAPE;
+  if (host_context_lens && partition_size == 0)
+    part = plan_partition(host_context_lens, num_seqs, num_heads, head_dim, max_context_len,
+                          workspace_bytes, workspace != nullptr);
 
   pa::DecodeParams p{};
   p.out = out;
@@ -116,7 +196,13 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
     p.part_ml = reinterpret_cast<float2 *>(base + w.ml_off);
     p.part_o = reinterpret_cast<float *>(base + w.o_off);
   }
-  return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype,
+  if (host_context_lens) {
+    pa::WorkList items, merge_rows;
+    if (plan_work(host_context_lens, num_seqs, max_context_len, part, &items, &merge_rows))
+      return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, &items,
+                                        &merge_rows, static_cast<hipStream_t>(stream)));
+  }
+  return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream)));
 }
 

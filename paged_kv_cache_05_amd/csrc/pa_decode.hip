@@ -376,18 +376,12 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   if (threadIdx.x == 0) p.part_ml[row * NP + part] = make_float2(M, lsum);
 }
 
-// One workgroup per (head, sequence, partition); the hardware dispatcher
-// hands slots to workgroups as earlier ones finish.
+// Workgroup for head h of sequence b, partition `part`: clamps the context
+// from the device array, writes a zero row for an empty context (partition
+// 0 only) and leaves at once when the partition holds no token.
 template <typename T, int D, int B, int W>
-__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
-  __shared__ ItemShared<T, D, W> sh;
-  // Partition index is the slowest grid dimension, counted down: the last
-  // partitions, which exist only for the longest sequences, are dispatched
-  // first and partition 0 (every row, including the short ones) last, so
-  // the work that trails the launch is the smallest.
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int part = p.num_partitions - 1 - (int)blockIdx.z;
+__device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
+                                           int b, int part) {
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
   if (ctx == 0) {
@@ -401,14 +395,35 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
   process_item<T, D, B, W>(p, sh, b, h, part, ctx);
 }
 
+// One workgroup per (head, sequence, partition); the hardware dispatcher
+// hands slots to workgroups as earlier ones finish.  The partition index is
+// the slowest grid dimension, counted down: the last partitions, which
+// exist only for the longest sequences, are dispatched first and partition
+// 0 (every row, including the short ones) last, so the work that trails
+// the launch is the smallest.
+template <typename T, int D, int B, int W>
+__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
+  __shared__ ItemShared<T, D, W> sh;
+  decode_one<T, D, B, W>(p, sh, blockIdx.x, blockIdx.y, p.num_partitions - 1 - (int)blockIdx.z);
+}
+
+// Workgroups own (head, listed item): the host listed the non-empty
+// (sequence, partition) items, longest first, so no workgroup is empty and
+// the smallest items trail the launch.
+template <typename T, int D, int B, int W>
+__global__ void __launch_bounds__(64 * W) decode_listed_kernel(const DecodeParams p,
+                                                                const WorkList items) {
+  __shared__ ItemShared<T, D, W> sh;
+  const uint32_t it = items.item[blockIdx.y];
+  decode_one<T, D, B, W>(p, sh, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu));
+}
+
 // Second pass, rows with several partitions only: out = sum_p w_p o_p /
-// sum_p w_p l_p with w_p = 2^(m_p - max_p m_p).  One workgroup per
-// (head, sequence); the partition results come from the first pass, made
-// visible by the kernel boundary.
+// sum_p w_p l_p with w_p = 2^(m_p - max_p m_p).  One workgroup of head_dim
+// threads per (head, sequence); the partition results come from the first
+// pass, made visible by the kernel boundary.
 template <typename T, int D>
-__global__ void __launch_bounds__(D) merge_kernel(const DecodeParams p) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+__device__ __forceinline__ void merge_one(const DecodeParams &p, int h, int b) {
   const size_t row = (size_t)b * p.num_heads + h;
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
@@ -431,37 +446,62 @@ __global__ void __launch_bounds__(D) merge_kernel(const DecodeParams p) {
   reinterpret_cast<T *>(p.out)[row * D + d] = T(num / den);
 }
 
+template <typename T, int D>
+__global__ void __launch_bounds__(D) merge_kernel(const DecodeParams p) {
+  merge_one<T, D>(p, blockIdx.x, blockIdx.y);
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(D) merge_listed_kernel(const DecodeParams p,
+                                                          const WorkList rows) {
+  merge_one<T, D>(p, blockIdx.x, (int)rows.item[blockIdx.y]);
+}
+
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 8
 #endif
 
+struct Lists {
+  const WorkList *items, *merge_rows;
+};
+
 template <typename T, int D, int B>
-hipError_t launch_typed(const DecodeParams &p, int num_seqs, hipStream_t stream) {
+hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_t stream) {
   constexpr int W = PA_DECODE_WAVES;  // waves per workgroup
-  const dim3 grid(p.num_heads, num_seqs, p.num_partitions);
-  decode_kernel<T, D, B, W><<<grid, 64 * W, 0, stream>>>(p);
+  if (l.items) {
+    if (l.items->count > 0)
+      decode_listed_kernel<T, D, B, W>
+          <<<dim3(p.num_heads, l.items->count), 64 * W, 0, stream>>>(p, *l.items);
+    if (p.num_partitions > 1 && l.merge_rows && l.merge_rows->count > 0)
+      merge_listed_kernel<T, D>
+          <<<dim3(p.num_heads, l.merge_rows->count), D, 0, stream>>>(p, *l.merge_rows);
+    return hipGetLastError();
+  }
+  decode_kernel<T, D, B, W>
+      <<<dim3(p.num_heads, num_seqs, p.num_partitions), 64 * W, 0, stream>>>(p);
   if (p.num_partitions > 1)
     merge_kernel<T, D><<<dim3(p.num_heads, num_seqs), D, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_block(const DecodeParams &p, int num_seqs, int block_size, hipStream_t s) {
+hipError_t launch_block(const DecodeParams &p, int num_seqs, int block_size, Lists l,
+                        hipStream_t s) {
   switch (block_size) {
-    case 8: return launch_typed<T, D, 8>(p, num_seqs, s);
-    case 16: return launch_typed<T, D, 16>(p, num_seqs, s);
-    case 32: return launch_typed<T, D, 32>(p, num_seqs, s);
-    case 64: return launch_typed<T, D, 64>(p, num_seqs, s);
+    case 8: return launch_typed<T, D, 8>(p, num_seqs, l, s);
+    case 16: return launch_typed<T, D, 16>(p, num_seqs, l, s);
+    case 32: return launch_typed<T, D, 32>(p, num_seqs, l, s);
+    case 64: return launch_typed<T, D, 64>(p, num_seqs, l, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_dim(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
-                      hipStream_t s) {
+                      Lists l, hipStream_t s) {
   switch (head_dim) {
-    case 64: return launch_block<T, 64>(p, num_seqs, block_size, s);
-    case 128: return launch_block<T, 128>(p, num_seqs, block_size, s);
+    case 64: return launch_block<T, 64>(p, num_seqs, block_size, l, s);
+    case 128: return launch_block<T, 128>(p, num_seqs, block_size, l, s);
   }
   return hipErrorInvalidValue;
 }
@@ -482,9 +522,11 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_di
 }
 
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
-                         int dtype, hipStream_t stream) {
-  if (dtype == 0) return launch_dim<_Float16>(p, num_seqs, head_dim, block_size, stream);
-  if (dtype == 1) return launch_dim<float>(p, num_seqs, head_dim, block_size, stream);
+                         int dtype, const WorkList *items, const WorkList *merge_rows,
+                         hipStream_t stream) {
+  const Lists l{items, merge_rows};
+  if (dtype == 0) return launch_dim<_Float16>(p, num_seqs, head_dim, block_size, l, stream);
+  if (dtype == 1) return launch_dim<float>(p, num_seqs, head_dim, block_size, l, stream);
   return hipErrorInvalidValue;
 }
 

@@ -34,9 +34,22 @@ struct WorkspaceLayout {
 WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_dim,
                                         int num_partitions);
 
-// dtype: 0 = f16, 1 = f32.  Returns the launch status.
+// A host-built work list, passed by value as kernel arguments (so it must
+// stay under the 4 KiB argument limit together with DecodeParams).  Each
+// entry packs (sequence << 16) | partition.
+constexpr int kMaxListed = 960;
+struct WorkList {
+  int count;
+  uint32_t item[kMaxListed];
+};
+
+// dtype: 0 = f16, 1 = f32.  `items` (optional) lists the (sequence,
+// partition) work items in launch order, `merge_rows` (optional, needed when
+// items is given and num_partitions > 1) the sequences that span several
+// partitions.  Returns the launch status.
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
-                         int dtype, hipStream_t stream);
+                         int dtype, const WorkList *items, const WorkList *merge_rows,
+                         hipStream_t stream);
 
 hipError_t launch_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
                            const int64_t *slot_mapping, int num_tokens, int num_heads,

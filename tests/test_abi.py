@@ -84,7 +84,8 @@ def decode_call(lib, **over):
     args = dict(out=OUT, q=Q, k_pool=KP, v_pool=VP, block_tables=TB, context_lens=CL,
                 num_seqs=4, num_heads=2, head_dim=64, block_size=16, num_blocks=32,
                 max_blocks_per_seq=4, max_context_len=50, scale=0.125, dtype=1,
-                partition_size=0, workspace=None, workspace_bytes=0, stream=None)
+                partition_size=0, host_context_lens=None, workspace=None, workspace_bytes=0,
+                stream=None)
     args.update(over)
     return lib.pa_decode(*args.values())
 

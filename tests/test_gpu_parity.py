@@ -51,7 +51,8 @@ def assert_close(gpu, ref, dtype, where=""):
                              f"gpu={gpu[tuple(i)]!r} oracle={ref[tuple(i)]!r}")
 
 
-def gpu_decode(pa, wl, k, v, device, partition_size=0, ctx=None, tables=None, workspace=None):
+def gpu_decode(pa, wl, k, v, device, partition_size=0, ctx=None, tables=None, workspace=None,
+               host_ctx=None):
     ctx = wl.context_lens if ctx is None else ctx
     tables = wl.block_tables if tables is None else tables
     N, H, D = wl.q.shape
@@ -60,8 +61,11 @@ def gpu_decode(pa, wl, k, v, device, partition_size=0, ctx=None, tables=None, wo
     maxctx = int(max(int(np.max(ctx)) if len(ctx) else 0, 1))
     if workspace is None:
         workspace = pa.new_workspace(N, H, D, maxctx, partition_size, device=device)
+    if host_ctx is not None:
+        maxctx = max(maxctx, int(np.max(host_ctx)))
+        workspace = pa.new_workspace(N, H, D, maxctx, partition_size, device=device)
     pa.pa_decode(out, q, k, v, dev(tables, device), dev(ctx, device), float(wl.scale), maxctx,
-                 partition_size=partition_size, workspace=workspace)
+                 partition_size=partition_size, workspace=workspace, host_context_lens=host_ctx)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -321,6 +325,54 @@ def test_write_skips_slots_outside_pool(pa, oracle_lib, device):
     ok, ov = k0.copy(), k0.copy()
     oracle_lib.write_kv(key[[0, 2]], key[[0, 2]], ok, ov, slots[[0, 2]])
     assert np.array_equal(tbits(k), bits(ok)) and np.array_equal(tbits(v), bits(ov))
+
+
+@pytest.mark.parametrize("config,kw,part", [
+    (1, {}, 16), (1, {}, 0), (2, {}, 0), (2, {}, 256), (2, {}, 1024), (3, {"block_size": 8}, 0),
+    (3, {"block_size": 32}, 64), (4, {}, 0), (4, {}, 128),
+    (2, {"num_seqs": 24, "num_heads": 8}, 48), (2, {"num_seqs": 3, "num_heads": 2}, 0),
+], ids=["cfg1-p16", "cfg1-auto", "cfg2-auto", "cfg2-p256", "cfg2-p1024", "cfg3-b8-auto",
+        "cfg3-b32-p64", "cfg4-auto", "cfg4-p128", "cfg2small-p48", "cfg2tiny-auto"])
+def test_host_planned_launch(pa, oracle_lib, device, config, kw, part):
+    """With host-side context lengths the library launches only the non-empty
+    (sequence, partition) items, long ones first.  With an explicit partition
+    size the results are bit-identical to the unplanned launch (same
+    per-partition reduction order); with partition_size 0 the library also
+    picks the partition size from the lengths."""
+    wl = workload(config, **kw)
+    k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
+    announce(f"{wl.name}: planned vs unplanned, partition {part}")
+    plain = gpu_decode(pa, wl, k, v, device, partition_size=part)
+    planned = gpu_decode(pa, wl, k, v, device, partition_size=part, host_ctx=wl.context_lens)
+    if part:
+        assert np.array_equal(bits(planned), bits(plain))
+    assert_close(planned, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
+
+
+def test_host_lengths_as_upper_bound(pa, oracle_lib, device):
+    """Host lengths may exceed the device ones (the extra items find nothing
+    to do); empty sequences still get zero rows."""
+    wl = workload(2, num_seqs=24, num_heads=8)
+    ctx = wl.context_lens.copy()
+    ctx[[3, 7]] = 0
+    host = np.minimum(ctx + np.random.default_rng(2).integers(0, 300, size=len(ctx)),
+                      wl.max_blocks_per_seq * wl.block_size).astype(np.int32)
+    announce("host lengths as upper bound")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device, ctx=ctx,
+                     partition_size=64, host_ctx=host)
+    ref = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, ctx, wl.scale)
+    assert np.array_equal(got[[3, 7]], np.zeros_like(got[[3, 7]]))
+    assert_close(got, ref, wl.dtype, "upper-bound host lengths")
+
+
+def test_host_plan_over_capacity_falls_back(pa, oracle_lib, device):
+    """More work items than one launch can list (960) use the unplanned grid."""
+    ctx = np.random.default_rng(9).integers(1, 90, size=1100)
+    wl = W._simple("many-seqs-planned", 9, W.F16, 2, 64, 16, ctx)
+    announce("planned launch over capacity")
+    got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
+                     partition_size=32, host_ctx=wl.context_lens)
+    assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, "over capacity")
 
 
 def test_nondefault_stream(pa, oracle_lib, device):
