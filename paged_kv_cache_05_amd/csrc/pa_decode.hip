@@ -25,8 +25,9 @@
 //  * Online softmax in base 2 (scale * log2 e folded into one multiply).
 //    Each lane row keeps its own running max / sum / accumulator for the
 //    tokens it sees (tokens congruent to it modulo the row count), so the hot
-//    loop has no cross-row traffic; rows and waves are merged once through
-//    LDS at the end with the usual max/sum rescaling.
+//    loop has no cross-row traffic.  At the end the rows of a wave are folded
+//    by a lane butterfly and the waves merged through LDS, both with the
+//    usual max/sum rescaling.
 //  * Masking of the ragged last tile is a select on scores and values, never
 //    a multiply by zero, so whatever sits in unused slots (NaN included)
 //    cannot reach the result.
@@ -150,10 +151,10 @@ struct RowState {
   float acc[kAcc];
 };
 
-// LDS of one workgroup: the W * kTokensPerGroup row states it merges.
+// LDS of one workgroup: one softmax state per wave, merged at the end.
 template <typename T, int D, int W>
 struct ItemShared {
-  static constexpr int kStates = W * Geometry<T, D>::kTokensPerGroup;
+  static constexpr int kStates = W;
   float m[kStates];
   float l[kStates];
   float o[kStates][D];
@@ -323,18 +324,34 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   }
   if (bad) st.l = NAN;  // a table entry outside the pool poisons the row
 
-  // Merge the W * kTPG row states of this workgroup.
-  {
-    const int sidx = wave * kTPG + trow;
+  // Fold the wave's lane rows together (butterfly over the row bits of the
+  // lane index): every lane ends with the wave's state for its chunk(s).
+#pragma unroll
+  for (int off = kLPT; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(st.m, off);
+    const float l2 = __shfl_xor(st.l, off);
+    const float mn = fmaxf(st.m, m2);
+    const float a = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mn);
+    const float a2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+    st.l = st.l * a + l2 * a2;
+#pragma unroll
+    for (int i = 0; i < G::kAcc; ++i) {
+      const float o2 = __shfl_xor(st.acc[i], off);
+      st.acc[i] = st.acc[i] * a + o2 * a2;
+    }
+    st.m = mn;
+  }
+  // Merge the W wave states of this workgroup.
+  if (trow == 0) {
     if (col == 0) {
-      sh.m[sidx] = st.m;
-      sh.l[sidx] = st.l;
+      sh.m[wave] = st.m;
+      sh.l[wave] = st.l;
     }
 #pragma unroll
     for (int k = 0; k < G::kChunksPerLane; ++k)
 #pragma unroll
       for (int i = 0; i < G::kPerChunk; ++i)
-        sh.o[sidx][(col + k * kLPT) * G::kPerChunk + i] = st.acc[k * G::kPerChunk + i];
+        sh.o[wave][(col + k * kLPT) * G::kPerChunk + i] = st.acc[k * G::kPerChunk + i];
   }
   __syncthreads();
 
