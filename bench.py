@@ -122,6 +122,12 @@ def main():
     # The step's scheduler knows every context length on the host; passing
     # them lets pa_decode launch only non-empty work items, largest first.
     host_ctx = None if args.no_host_lengths else wl.context_lens
+    part = pa.pa_decode_partition_size(N, H, D, maxctx, args.partition, host_ctx,
+                                       ws.numel() if ws is not None else 0)
+    merges = -(-maxctx // part) > 1
+    kernel = ("decode_listed_kernel" if host_ctx is not None else "decode_kernel") + \
+        f"<{'f16' if wl.dtype == W.F16 else 'f32'},{D},{B},8>" + \
+        (" + merge_kernel" if merges else "")
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -210,7 +216,7 @@ def main():
             "context_lens": "lognormal median 300 sigma 0.9 clipped [1,2048]",
             "sum_context": int(wl.context_lens.sum()), "max_context": maxctx,
             "num_blocks": wl.num_blocks, "layer_pools_rotated": L,
-            "partition_size": args.partition or pa.default_partition(maxctx),
+            "partition_size": part,
             "host_planned_launch": host_ctx is not None,
         },
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
@@ -225,7 +231,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "pa_decode call: decode_kernel<f16,128,16,8> + merge_kernel<f16,128>",
+            "kernel": kernel,
         },
         "cpu_baseline": cpu,
         "parity_layer0_vs_oracle": parity,

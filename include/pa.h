@@ -82,6 +82,18 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim,
                                  int max_context_len, int partition_size);
 
 /*
+ * The partition length pa_decode uses for these arguments: partition_size
+ * when it is non-zero; else, with host_context_lens (HOST memory, may be
+ * NULL), the length it plans from them within workspace_bytes; else the
+ * default above.  A caller that wants the planner's free choice sizes the
+ * workspace with pa_decode_workspace_bytes(..., 256).  Returns a negative
+ * PA_ERR_* code for invalid arguments.
+ */
+int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int num_heads,
+                             int head_dim, int max_context_len, int partition_size,
+                             size_t workspace_bytes);
+
+/*
  * Single-query paged decode attention ([zhai] "method" paragraph, the
  * block-wise equation for A_ij and o_i; [rice] 3.3: per-block scores, the
  * softmax completed by a final reduction; [wywy] WHERE: the kernel fetches

@@ -35,8 +35,8 @@ def default_partition(max_context_len: int) -> int:
     return PA_LONG_PARTITION if max_context_len > PA_LONG_CONTEXT else PA_DEFAULT_PARTITION
 
 # Every symbol include/pa.h declares.
-EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_write_kv", "pa_copy_blocks",
-           "pa_status_string")
+EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
+           "pa_copy_blocks", "pa_status_string")
 
 
 class PAError(RuntimeError):
@@ -61,6 +61,8 @@ def library() -> ctypes.CDLL:
     lib.pa_decode.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = sz
+    lib.pa_decode_partition_size.argtypes = [vp, i32, i32, i32, i32, i32, sz]
+    lib.pa_decode_partition_size.restype = i32
     lib.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_write_kv.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
@@ -114,6 +116,22 @@ def pa_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
                                             int(max_context_len), int(partition_size))
     if n == ctypes.c_size_t(-1).value:
         raise PAError("pa_decode_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def pa_decode_partition_size(num_seqs, num_heads, head_dim, max_context_len, partition_size=0,
+                             host_context_lens=None, workspace_bytes=0) -> int:
+    """The partition length pa_decode will use for these arguments."""
+    import numpy as np
+    host = None
+    if host_context_lens is not None:
+        host = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+    n = library().pa_decode_partition_size(None if host is None else host.ctypes.data,
+                                           int(num_seqs), int(num_heads), int(head_dim),
+                                           int(max_context_len), int(partition_size),
+                                           int(workspace_bytes))
+    if n < 0:
+        raise PAError(f"pa_decode_partition_size: {pa_status_string(n)} ({n})")
     return int(n)
 
 

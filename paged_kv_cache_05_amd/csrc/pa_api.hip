@@ -150,6 +150,19 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
   return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, np).total;
 }
 
+int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int num_heads,
+                             int head_dim, int max_context_len, int partition_size,
+                             size_t workspace_bytes) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  const int part = effective_partition(partition_size, max_context_len);
+  if (!valid_partition(part)) return PA_ERR_SHAPE;
+  if (host_context_lens && partition_size == 0)
+    return plan_partition(host_context_lens, num_seqs, num_heads, head_dim, max_context_len,
+                          workspace_bytes, workspace_bytes > 0);
+  return part;
+}
+
 int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
               const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
               int num_heads, int head_dim, int block_size, int num_blocks,

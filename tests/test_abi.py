@@ -67,6 +67,31 @@ def test_workspace_bytes(pa):
             pa.pa_decode_workspace_bytes(*bad)
 
 
+def test_partition_size_query(pa):
+    """The partition length pa_decode uses: explicit, default, or planned
+    from host lengths within the workspace (host-only logic)."""
+    import numpy as np
+    q = pa.pa_decode_partition_size
+    assert q(64, 40, 128, 2048, 512) == 512
+    assert q(64, 40, 128, 2048) == pa.PA_DEFAULT_PARTITION
+    assert q(32, 96, 128, 16384) == pa.PA_LONG_PARTITION
+    # many rows: the plan keeps long partitions (no merge needed below 4096 tokens)
+    ctx = np.full(64, 2000, np.int32)
+    assert q(64, 40, 128, 2048, host_context_lens=ctx) == 4096
+    # few rows, long contexts: the plan splits them, as far as the workspace allows
+    few = np.full(2, 60000, np.int32)
+    ws256 = pa.pa_decode_workspace_bytes(2, 4, 128, 60000, 256)
+    assert q(2, 4, 128, 60000, host_context_lens=few, workspace_bytes=ws256) == 256
+    ws1024 = pa.pa_decode_workspace_bytes(2, 4, 128, 60000, 1024)
+    assert q(2, 4, 128, 60000, host_context_lens=few, workspace_bytes=ws1024) == 1024
+    assert q(2, 4, 128, 60000, host_context_lens=few, workspace_bytes=0) == 4096
+    # enough items at 4096 tokens: no further splitting
+    wide = np.full(600, 8000, np.int32)
+    assert q(600, 8, 128, 8000, host_context_lens=wide, workspace_bytes=ws256) == 4096
+    with pytest.raises(pa.PAError):
+        q(4, 4, 96, 100)
+
+
 # ---------------------------------------------------------------------------
 # host validation (fake device addresses; never run with a GPU visible)
 # ---------------------------------------------------------------------------
