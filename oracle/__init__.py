@@ -52,6 +52,24 @@ def build(force: bool = True) -> str:
     return LIBRARY
 
 
+def _bind(lib):
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_half_to_double_array.argtypes = [vp, vp, i64]
+    lib.oracle_half_to_double_array.restype = None
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, vp, i32, vp, i32, i32]
+    lib.oracle_decode.restype = i32
+    lib.oracle_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
+    lib.oracle_write_kv.restype = i32
+    lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
+    lib.oracle_copy_blocks.restype = i32
+    lib.oracle_threads_available.argtypes = []
+    lib.oracle_threads_available.restype = i32
+    return lib
+
+
 _lib = None
 
 
@@ -60,22 +78,7 @@ def _load():
     if _lib is None:
         if not os.path.exists(LIBRARY):
             build()
-        lib = ctypes.CDLL(LIBRARY)
-        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
-        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
-        lib.oracle_half_to_double.restype = ctypes.c_double
-        lib.oracle_half_to_double_array.argtypes = [vp, vp, i64]
-        lib.oracle_half_to_double_array.restype = None
-        lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                      f32, i32, vp, i32, vp, i32, i32]
-        lib.oracle_decode.restype = i32
-        lib.oracle_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32]
-        lib.oracle_write_kv.restype = i32
-        lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
-        lib.oracle_copy_blocks.restype = i32
-        lib.oracle_threads_available.argtypes = []
-        lib.oracle_threads_available.restype = i32
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(LIBRARY))
     return _lib
 
 
@@ -96,20 +99,20 @@ def _check(rc: int, what: str):
         raise OracleError(f"{what}: {_STATUS.get(rc, rc)}")
 
 
-def threads_available() -> int:
-    return int(_load().oracle_threads_available())
+def threads_available(_lib_=None) -> int:
+    return int((_lib_ or _load()).oracle_threads_available())
 
 
-def half_to_double(bits: np.ndarray) -> np.ndarray:
+def half_to_double(bits: np.ndarray, _lib_=None) -> np.ndarray:
     """Decode uint16 binary16 bit patterns to float64 with the oracle's own decoder."""
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     out = np.empty(bits.shape, dtype=np.float64)
-    _load().oracle_half_to_double_array(_ptr(bits), _ptr(out), bits.size)
+    (_lib_ or _load()).oracle_half_to_double_array(_ptr(bits), _ptr(out), bits.size)
     return out
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale, *,
-           pairs=None, return_weights=False, threads=0):
+           pairs=None, return_weights=False, threads=0, _lib_=None):
     """fp64 paged decode attention.
 
     q: [N][H][D]; pools: [NB][H][B][D] (float16 or float32, same type as q);
@@ -144,14 +147,14 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, *,
     if return_weights:
         wstride = max(int(ctx.max()) if N else 0, 1)
         w = np.full((N, H, wstride), np.nan, dtype=np.float64)
-    rc = _load().oracle_decode(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(tables),
+    rc = (_lib_ or _load()).oracle_decode(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(tables),
                                _ptr(ctx), N, H, D, B, NB, MB, float(np.float32(scale)), dt,
                                _ptr(pair_arr), npairs, _ptr(w), wstride, int(threads))
     _check(rc, "oracle decode")
     return (out, w) if return_weights else out
 
 
-def write_kv(key, value, k_pool, v_pool, slot_mapping):
+def write_kv(key, value, k_pool, v_pool, slot_mapping, _lib_=None):
     """Scatter key/value [T][H][D] into the pools in place (bit copies)."""
     key = np.ascontiguousarray(key)
     value = np.ascontiguousarray(value)
@@ -162,18 +165,43 @@ def write_kv(key, value, k_pool, v_pool, slot_mapping):
     dt = _dtype_code(key)
     T, H, D = key.shape
     NB, _, B, _ = k_pool.shape
-    rc = _load().oracle_write_kv(_ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slots),
+    rc = (_lib_ or _load()).oracle_write_kv(_ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slots),
                                  T, H, D, B, NB, dt)
     _check(rc, "oracle write_kv")
 
 
-def copy_blocks(k_pool, v_pool, block_mapping):
+def copy_blocks(k_pool, v_pool, block_mapping, _lib_=None):
     """Copy whole physical blocks src -> dst in both pools, in place."""
     pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
     for p in (k_pool, v_pool):
         if not p.flags.c_contiguous:
             raise OracleError("pools must be C-contiguous (written in place)")
     NB, H, B, D = k_pool.shape
-    rc = _load().oracle_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
+    rc = (_lib_ or _load()).oracle_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
                                     H, D, B, NB, _dtype_code(k_pool))
     _check(rc, "oracle copy_blocks")
+
+
+class Oracle:
+    """The same functions bound to another build of the oracle source (the
+    tests use it to check that their pins catch planted mistakes)."""
+
+    OracleError = OracleError
+
+    def __init__(self, library_path: str):
+        self._lib = _bind(ctypes.CDLL(library_path))
+
+    def half_to_double(self, bits):
+        return half_to_double(bits, _lib_=self._lib)
+
+    def decode(self, *args, **kw):
+        return decode(*args, _lib_=self._lib, **kw)
+
+    def write_kv(self, *args):
+        return write_kv(*args, _lib_=self._lib)
+
+    def copy_blocks(self, *args):
+        return copy_blocks(*args, _lib_=self._lib)
+
+    def threads_available(self):
+        return threads_available(_lib_=self._lib)
