@@ -17,6 +17,10 @@ pa_decode call (one kernel launch each), after W untimed warm-up steps.
 
 Also times the CPU oracle on the host (the full batch of layer 0, all host
 threads) as a reported baseline, and checks sampled GPU rows against it.
+
+``--workload generation`` instead times the multi-step decoding loop that
+the host block manager drives (parallel sampling with beam-like pruning at
+the same layer shape, every step over all L layers) and prints its own line.
 """
 import argparse
 import hashlib
@@ -79,6 +83,118 @@ def calibrate_copy():
     return 0
 
 
+def bench_generation(args):
+    """Decoding loop driven by the host block manager: 16 prompts (lengths
+    lognormal, median 300, clipped [1, 2048]) x 4 parallel samples sharing
+    each prompt's blocks, 40 heads x head_dim 128, fp16, B = 16; before a
+    step, with probability 1/4, one sample is pruned and another sample of
+    its prompt forked in its place.  A step = the manager's decisions and
+    their upload (once), then for each of L layers: copy-on-write copies,
+    KV write, paged decode.  Model GEMMs are not part of this path."""
+    import torch
+
+    import paged_kv_cache_05_amd as pa
+    from paged_kv_cache_05_amd import manager as M
+    import workloads as W
+
+    device = torch.device("cuda:0")
+    L, K, Wm = args.layers, args.steps, args.warmup
+    rng = np.random.default_rng(21)
+    plens = W.lognormal_lengths(rng, 16)
+    g = W.generation(seed=21, dtype=W.F16, num_heads=40, head_dim=128, block_size=16,
+                     prompt_lens=tuple(int(x) for x in plens), samples=4, steps=Wm + K,
+                     churn=0.25)
+    H, D, B = g.num_heads, g.head_dim, g.block_size
+    shape = (g.num_blocks, H, B, D)
+    pools = [tuple(torch.full(shape, float("nan"), dtype=torch.float16, device=device)
+                   for _ in range(2)) for _ in range(L)]
+    m = M.BlockManager(g.num_blocks, B)
+    stepper = M.DecodeStepper(m, pools, g.max_blocks, args.partition)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    for p, (pk, pv) in enumerate(zip(g.prompt_keys, g.prompt_values)):
+        m.add(p)
+        slots, _ = m.append([p] * len(pk))
+        dk, dv, ds = to(pk), to(pv), to(slots)
+        for k, v in pools:
+            pa.pa_write_kv(dk, dv, k, v, ds)
+    inputs = [(to(st.key), to(st.value), to(st.q)) for st in g.steps]
+    outs = [torch.empty_like(x[2]) for x in inputs]
+    scale = float(g.scale)
+    stream = torch.cuda.current_stream()
+    host_s, mgr_s, copies, tokens, dec_bytes, blocks_used, private_need = [], [], 0, 0, 0, [], []
+    evs = []
+
+    def one(i, timed):
+        nonlocal copies, tokens, dec_bytes
+        st = g.steps[i]
+        t = time.perf_counter()
+        for s_ in st.frees:
+            m.free(s_)
+        for parent, child in st.forks:
+            m.fork(parent, child)
+        plan = stepper.plan(st.seqs)
+        if timed:
+            host_s.append(time.perf_counter() - t)
+            mgr_s.append(plan.host_seconds)
+            copies += len(plan.pairs)
+            tokens += len(st.seqs)
+            dec_bytes += L * W.algorithmic_bytes(plan.context_lens, H, D, B, 2)
+            blocks_used.append(g.num_blocks - m.num_free)
+            private_need.append(int(sum(-(-int(c) // B) for c in plan.context_lens)))
+        key, value, q = inputs[i]
+        for layer in range(L):
+            if timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            stepper.layer(plan, layer, key, value, q, scale, outs[i])
+            if timed:
+                b.record(stream)
+                evs.append((a, b))
+
+    for i in range(Wm):
+        one(i, False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(Wm, Wm + K):
+        one(i, True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t0.elapsed_time(t1)
+    layer_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    for o in outs[Wm:]:
+        if not torch.isfinite(o).all():
+            raise SystemExit("bench: non-finite output in the generation loop")
+    ms_per_step = total_ms / K
+    rec = {
+        "metric": "decode-loop attention tokens/s (block manager + COW + KV write + paged "
+                  "decode, all layers)",
+        "value": round(tokens / (total_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded; lognormal prompt lengths, N(0,1) q/K/V)",
+        "config": {"workload": f"parallel sampling 16 prompts x 4 samples, OPT-13B-shaped "
+                               f"attention, {L} layers per step",
+                   "num_heads": H, "head_dim": D, "block_size": B, "layers": L,
+                   "prompt_lens_sum": int(sum(plens)), "num_blocks": g.num_blocks},
+        "host_manager_us_mean": round(1e6 * float(np.mean(mgr_s)), 2),
+        "host_manager_us_p90": round(1e6 * float(np.percentile(mgr_s, 90)), 2),
+        "host_plan_incl_staging_wait_us_mean": round(1e6 * float(np.mean(host_s)), 2),
+        "wall_ms_per_step": round(1e3 * wall / K, 5),
+        "layer_ms_mean": round(float(layer_ms.mean()), 5),
+        "layer_attention_GBps": round(dec_bytes / (L * K) / (float(layer_ms.mean()) * 1e-3) / 1e9, 1),
+        "cow_copies_per_step": round(copies / K, 3),
+        "blocks_in_use_final": blocks_used[-1],
+        "blocks_if_private_final": private_need[-1],
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +207,9 @@ def main():
                     help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--workload", choices=["decode", "generation"], default="decode",
+                    help="decode: one layer's decode step (the default line); generation: the "
+                         "block-manager decoding loop over all layers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus "
@@ -99,6 +218,8 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.workload == "generation":
+        return bench_generation(args)
 
     import torch
 

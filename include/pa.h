@@ -16,7 +16,8 @@
  *  - Every pointer argument is device memory owned by the caller (except
  *    `stream`, a hipStream_t, and the return of pa_status_string).  The
  *    library allocates nothing, frees nothing and keeps no state between
- *    calls.  It is thread-safe.
+ *    calls apart from a per-thread error description (pa_last_error).  It
+ *    is thread-safe.
  *  - Work is enqueued asynchronously on `stream` (NULL = the default stream);
  *    no call synchronises.  Buffers must stay valid until the work completes.
  *  - Element type codes: PA_F16 (IEEE binary16) or PA_F32.  Query, pools,
@@ -191,6 +192,18 @@ int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
 
 /* Static, NUL-terminated description of a status code. */
 const char *pa_status_string(int status);
+
+/*
+ * Describes the last HIP runtime error this library saw on the calling
+ * thread: the error of a launch that returned PA_ERR_HIP (HIP's error name
+ * and text), or an error an earlier HIP call on the thread had left pending,
+ * which a launch clears before it starts (hipGetLastError reports the last
+ * failure of any call on the thread, so the status read after a launch would
+ * otherwise not be the launch's own).  "" when there was none.  The string
+ * belongs to the library, stays valid until the thread's next call into it,
+ * and is not cleared by reading it.
+ */
+const char *pa_last_error(void);
 
 #ifdef __cplusplus
 }

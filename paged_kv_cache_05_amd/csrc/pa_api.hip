@@ -3,10 +3,12 @@
 // include/pa.h; this file checks scalars and pointers only and never reads
 // device memory.
 #include <math.h>
+#include <stdio.h>
 
 #include <algorithm>
 
-#include "../../include/pa.h"
+#include "pa.h"
+#include "pa_manager.h"
 #include "pa_kernels.h"
 
 namespace {
@@ -47,7 +49,30 @@ int num_partitions(int max_context_len, int part) {
   return max_context_len <= 0 ? 1 : (max_context_len + part - 1) / part;
 }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+// Description of the last HIP error this library saw on the calling thread.
+thread_local char t_detail[384] = "";
+
+// hipGetLastError reports the last failure of any HIP call on the thread,
+// so a launch first takes whatever an earlier call (of the caller, or of a
+// framework around it) left behind; the status read after the launch then
+// belongs to the launch.  Both are described for pa_last_error.
+template <class Launch>
+int launch_checked(const char *what, Launch &&launch) {
+  const hipError_t stale = hipGetLastError();
+  const hipError_t e = launch();
+  if (e != hipSuccess) {
+    snprintf(t_detail, sizeof t_detail, "%s: %s (%s)%s%s", what, hipGetErrorName(e),
+             hipGetErrorString(e),
+             stale != hipSuccess ? "; an earlier HIP call on this thread had failed with " : "",
+             stale != hipSuccess ? hipGetErrorName(stale) : "");
+  } else if (stale != hipSuccess) {
+    snprintf(t_detail, sizeof t_detail,
+             "%s launched; it cleared the error %s (%s) that an earlier HIP call on this "
+             "thread had left",
+             what, hipGetErrorName(stale), hipGetErrorString(stale));
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
 
 int clamp_ctx(int32_t c, int max_context_len) {
   return c < 0 ? 0 : (c > max_context_len ? max_context_len : c);
@@ -127,6 +152,8 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 
 extern "C" {
 
+const char *pa_last_error(void) { return t_detail; }
+
 const char *pa_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -135,6 +162,9 @@ const char *pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error at launch";
+    case PA_ERR_NO_SEQUENCE: return "no sequence with that id";
+    case PA_ERR_EXISTS: return "a sequence with that id already exists";
+    case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
   }
   return "unknown status";
 }
@@ -212,11 +242,15 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   if (host_context_lens) {
     pa::WorkList items, merge_rows;
     if (plan_work(host_context_lens, num_seqs, max_context_len, part, &items, &merge_rows))
-      return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, &items,
-                                        &merge_rows, static_cast<hipStream_t>(stream)));
+      return launch_checked("pa_decode", [&] {
+        return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, &items, &merge_rows,
+                                 static_cast<hipStream_t>(stream));
+      });
   }
-  return from_hip(pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr,
-                                    static_cast<hipStream_t>(stream)));
+  return launch_checked("pa_decode", [&] {
+    return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr,
+                             static_cast<hipStream_t>(stream));
+  });
 }
 
 int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
@@ -230,9 +264,11 @@ int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)slot_mapping & 7u))
     return PA_ERR_SHAPE;
-  return from_hip(pa::launch_write_kv(key, value, k_pool, v_pool, slot_mapping, num_tokens,
-                                      num_heads, head_dim * elem_bytes(dtype), block_size,
-                                      num_blocks, static_cast<hipStream_t>(stream)));
+  return launch_checked("pa_write_kv", [&] {
+    return pa::launch_write_kv(key, value, k_pool, v_pool, slot_mapping, num_tokens, num_heads,
+                               head_dim * elem_bytes(dtype), block_size, num_blocks,
+                               static_cast<hipStream_t>(stream));
+  });
 }
 
 int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping, int num_pairs,
@@ -246,8 +282,10 @@ int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping, int
   if (!aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)block_mapping & 7u))
     return PA_ERR_SHAPE;
   const size_t block_bytes = (size_t)num_heads * block_size * head_dim * elem_bytes(dtype);
-  return from_hip(pa::launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
-                                         num_blocks, static_cast<hipStream_t>(stream)));
+  return launch_checked("pa_copy_blocks", [&] {
+    return pa::launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs, block_bytes,
+                                  num_blocks, static_cast<hipStream_t>(stream));
+  });
 }
 
 }  // extern "C"

@@ -11,12 +11,16 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_exports(pa):
@@ -44,10 +48,19 @@ def test_header_constants_match_binding(pa):
 
 
 def test_status_strings(pa):
-    for code in range(0, -6, -1):
+    for code in range(0, -9, -1):
         s = pa.pa_status_string(code)
         assert s and s != "unknown status"
     assert pa.pa_status_string(-99) == "unknown status"
+
+
+def test_last_error_starts_empty(pa):
+    import threading
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(pa.pa_last_error()))
+    t.start()
+    t.join()
+    assert seen == [""]
 
 
 def test_workspace_bytes(pa):
@@ -167,3 +180,17 @@ def test_write_and_copy_reject(pa):
     assert c(block_mapping=None) == -1 and c(v_pool=None) == -1
     assert c(head_dim=100) == -3 and c(num_pairs=-2) == -2 and c(k_pool=KP + 8) == -2
     assert c(num_pairs=0, block_mapping=None) == 0
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before torch must not map a second HIP runtime
+    (torch bundles its own under the same soname; two runtimes in one process
+    do not share devices, memory or streams)."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_05_amd as pa; pa.library(); import torch; "
+            "print(len(pa.hip_runtimes()))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

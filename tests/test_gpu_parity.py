@@ -389,3 +389,34 @@ def test_nondefault_stream(pa, oracle_lib, device):
         pa.pa_decode(out, q, k, v, tabs, ctx, float(wl.scale), wl.max_context_len, workspace=ws)
     s.synchronize()
     assert_close(out.cpu().numpy(), oracle_decode(oracle_lib, wl), wl.dtype, "stream")
+
+
+def test_pending_runtime_error_is_not_taken_for_the_launch(pa, oracle_lib, device):
+    """An error an earlier HIP call left pending on the thread (here
+    hipGetDevice(NULL): hipErrorInvalidValue, no side effect) does not make
+    the next launch report failure; pa_last_error names it.  The C entry
+    point is called directly so that no other HIP call comes in between."""
+    import ctypes
+    runtimes = pa.hip_runtimes()
+    assert len(runtimes) == 1
+    hip = ctypes.CDLL(runtimes[0])
+    hip.hipGetDevice.argtypes = [ctypes.c_void_p]
+    wl = workload(1)
+    k, v = dev(wl.k_pool_pre, device), dev(wl.v_pool_pre, device)
+    key, val = dev(wl.new_key, device), dev(wl.new_value, device)
+    slots = dev(wl.slot_mapping, device)
+    stream = torch.cuda.current_stream().cuda_stream
+    T, H, D = wl.new_key.shape
+    NB, _, B, _ = wl.k_pool_pre.shape
+    dt = pa.PA_F16 if wl.dtype == W.F16 else pa.PA_F32
+    lib = pa.library()
+    torch.cuda.synchronize()
+    assert hip.hipGetDevice(None) != 0          # leaves the error pending
+    rc = lib.pa_write_kv(key.data_ptr(), val.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         slots.data_ptr(), T, H, D, B, NB, dt, stream)
+    assert rc == pa.PA_OK, pa.pa_last_error()
+    assert "hipErrorInvalidValue" in pa.pa_last_error()
+    torch.cuda.synchronize()
+    ref_k, ref_v = wl.k_pool_pre.copy(), wl.v_pool_pre.copy()
+    oracle_lib.write_kv(wl.new_key, wl.new_value, ref_k, ref_v, wl.slot_mapping)
+    assert np.array_equal(tbits(k), bits(ref_k)) and np.array_equal(tbits(v), bits(ref_v))

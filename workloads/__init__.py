@@ -473,3 +473,96 @@ def device_pools(wl: Workload, device, seed_offset=0, chunk_blocks=2048):
             pool[sel] = vals
         pools.append(pool)
     return pools[0], pools[1]
+
+
+# ---------------------------------------------------------------------------
+# Multi-step generation: the input program of a decoding loop driven by a
+# block manager.  Only ids, events and values are drawn here; where each
+# token lands is the manager's decision.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class GenStep:
+    frees: list                      # sequence ids dropped before the step (pruned)
+    forks: list                      # (parent, child) pairs made before the step
+    seqs: list                       # the step's batch, in order
+    key: np.ndarray                  # [n][H][D] the new token of each sequence
+    value: np.ndarray
+    q: np.ndarray                    # [n][H][D]
+
+
+@dataclass
+class Generation:
+    name: str
+    seed: int
+    dtype: str
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks: int                  # block-table width that fits every sequence
+    scale: np.float32
+    prompt_keys: list                # per prompt, [L][H][D]; prompt p is sequence p
+    prompt_values: list
+    steps: list                      # GenStep per decoding step
+
+
+def generation(seed=11, dtype=F16, num_heads=4, head_dim=128, block_size=16,
+               prompt_lens=(37, 5, 64, 100, 1), samples=3, steps=24, churn=0.25):
+    """Parallel sampling with beam-like pruning.
+
+    Each prompt is written, then forked into ``samples`` sequences that share
+    its blocks (the prompt's own id is the first sample).  Every decoding
+    step appends one token to every live sequence.  Before a step, with
+    probability ``churn`` one live sequence is dropped and another live
+    sequence of the same prompt is forked in its place (a beam candidate
+    replaced by a copy of a better one), so forks also happen from sequences
+    whose last block is partly filled and both sides then write into it.
+    """
+    rng = np.random.default_rng(seed)
+    dt = NP_DTYPES[dtype]
+    H, D, B = num_heads, head_dim, block_size
+    P = len(prompt_lens)
+    prompt_keys = [_normal(rng, (int(L), H, D), dt) for L in prompt_lens]
+    prompt_values = [_normal(rng, (int(L), H, D), dt) for L in prompt_lens]
+    group = {p: p for p in range(P)}           # sequence id -> prompt
+    live = list(range(P))
+    next_id = P
+    length = {p: int(L) for p, L in enumerate(prompt_lens)}
+    peak_blocks = 0
+    out = []
+    for t in range(steps):
+        frees, forks = [], []
+        if t == 0:
+            for p in range(P):
+                for _ in range(samples - 1):
+                    forks.append((p, next_id))
+                    group[next_id] = p
+                    length[next_id] = length[p]
+                    live.append(next_id)
+                    next_id += 1
+        elif rng.random() < churn:
+            victim = live[int(rng.integers(len(live)))]
+            mates = [s for s in live if group[s] == group[victim] and s != victim]
+            if mates:
+                parent = mates[int(rng.integers(len(mates)))]
+                live.remove(victim)
+                frees.append(victim)
+                forks.append((parent, next_id))
+                group[next_id] = group[parent]
+                length[next_id] = length[parent]
+                live.append(next_id)
+                next_id += 1
+        n = len(live)
+        out.append(GenStep(frees=frees, forks=forks, seqs=list(live),
+                           key=_normal(rng, (n, H, D), dt), value=_normal(rng, (n, H, D), dt),
+                           q=_normal(rng, (n, H, D), dt)))
+        for s in live:
+            length[s] += 1
+        # upper bound on blocks in use: every sequence privately owning its blocks
+        peak_blocks = max(peak_blocks, sum(_blocks_for(length[s], B) for s in live))
+    max_len = max(length.values())
+    return Generation(name="generation", seed=seed, dtype=dtype, num_heads=H, head_dim=D,
+                      block_size=B, num_blocks=peak_blocks + P + 4,
+                      max_blocks=_blocks_for(max_len, B), scale=np.float32(1.0 / math.sqrt(D)),
+                      prompt_keys=prompt_keys, prompt_values=prompt_values, steps=out)
