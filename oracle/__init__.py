@@ -16,6 +16,10 @@ What each function follows on the pages (Kwon et al., PagedAttention):
   "KV cache manager" (next free position of the last block).
 * :func:`copy_blocks` -- wywy.jp WHERE, parallel-sampling copy-on-write
   example; zhaifeiyue memory-management table, "Copy-on-Write".
+* :func:`swap_blocks` -- wywy.jp Keyword "Swapping" and Overview,
+  scheduling and preemption (every block of an evicted sequence goes to CPU
+  memory and comes back whole); zhaifeiyue "Scheduling & Preemption" table,
+  row "Swap".
 """
 from __future__ import annotations
 
@@ -65,6 +69,8 @@ def _bind(lib):
     lib.oracle_write_kv.restype = i32
     lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
     lib.oracle_copy_blocks.restype = i32
+    lib.oracle_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
+    lib.oracle_swap_blocks.restype = i32
     lib.oracle_threads_available.argtypes = []
     lib.oracle_threads_available.restype = i32
     return lib
@@ -182,6 +188,27 @@ def copy_blocks(k_pool, v_pool, block_mapping, _lib_=None):
     _check(rc, "oracle copy_blocks")
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, _lib_=None):
+    """Copy block src of the source pools onto block dst of the destination
+    pools for every (src, dst) pair, K and V (swap out or in)."""
+    pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    for p in (dst_k, dst_v):
+        if not p.flags.c_contiguous:
+            raise OracleError("destination pools must be C-contiguous (written in place)")
+    src_k = np.ascontiguousarray(src_k)
+    src_v = np.ascontiguousarray(src_v)
+    sNB, H, B, D = src_k.shape
+    dNB = dst_k.shape[0]
+    if dst_k.shape[1:] != (H, B, D) or src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+        raise OracleError("pools differ in block shape")
+    dt = _dtype_code(src_k)
+    if _dtype_code(dst_k) != dt:
+        raise OracleError("pools differ in element type")
+    rc = (_lib_ or _load()).oracle_swap_blocks(_ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v),
+                                               _ptr(pairs), pairs.shape[0], H, D, B, sNB, dNB, dt)
+    _check(rc, "oracle swap_blocks")
+
+
 class Oracle:
     """The same functions bound to another build of the oracle source (the
     tests use it to check that their pins catch planted mistakes)."""
@@ -202,6 +229,9 @@ class Oracle:
 
     def copy_blocks(self, *args):
         return copy_blocks(*args, _lib_=self._lib)
+
+    def swap_blocks(self, *args):
+        return swap_blocks(*args, _lib_=self._lib)
 
     def threads_available(self):
         return threads_available(_lib_=self._lib)

@@ -28,6 +28,12 @@
  *    physical block's contents into a newly allocated one (wywy.jp, WHERE,
  *    parallel-sampling example with physical blocks 1 and 3; zhaifeiyue,
  *    memory-management table, "Copy-on-Write"; ricepunchb section 5.1).
+ *  - swap_blocks: swapping, the recovery that moves every KV block of an
+ *    evicted sequence from GPU memory to CPU memory and back whole when it
+ *    resumes (wywy.jp, Keyword "Swapping" and "All-or-nothing eviction",
+ *    Overview, scheduling and preemption; zhaifeiyue, "Scheduling &
+ *    Preemption" table, row "Swap"): each listed block of one pool pair is
+ *    copied onto a block of another pool pair of the same shape per block.
  *
  * Readings taken where the pages are silent or garbled:
  *  - token t (0-based) of a sequence lives in logical block t div B at offset
@@ -340,6 +346,43 @@ int oracle_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
         const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
         memcpy((char *)k_pool + dst * block_bytes, (const char *)k_pool + src * block_bytes, block_bytes);
         memcpy((char *)v_pool + dst * block_bytes, (const char *)v_pool + src * block_bytes, block_bytes);
+    }
+    return ORC_OK;
+}
+
+/*
+ * For each (src, dst) pair copy every element (head, offset, dim) of block
+ * src of the source pools onto block dst of the destination pools, K and V.
+ * The two pool pairs may hold different numbers of blocks (src_NB, dst_NB)
+ * and must not overlap.  Destinations must be distinct; a source may be
+ * listed more than once.
+ */
+int oracle_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                       const int64_t *block_mapping, int num_pairs, int H, int D, int B,
+                       int src_NB, int dst_NB, int dtype)
+{
+    const int es = elem_bytes(dtype);
+    if (!dst_k || !dst_v || !src_k || !src_v || (num_pairs > 0 && !block_mapping) ||
+        num_pairs < 0 || !es)
+        return ORC_BAD_ARG;
+    for (int i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || src >= src_NB || dst < 0 || dst >= dst_NB)
+            return ORC_BAD_PAIRS;
+        for (int k = 0; k < i; ++k)
+            if (block_mapping[2 * k + 1] == dst)
+                return ORC_BAD_PAIRS;
+    }
+    for (int i = 0; i < num_pairs; ++i) {
+        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        for (int h = 0; h < H; ++h)
+            for (int o = 0; o < B; ++o)
+                for (int d = 0; d < D; ++d) {
+                    const int64_t from = pool_index(src, h, o, d, H, B, D);
+                    const int64_t to = pool_index(dst, h, o, d, H, B, D);
+                    memcpy((char *)dst_k + to * es, (const char *)src_k + from * es, es);
+                    memcpy((char *)dst_v + to * es, (const char *)src_v + from * es, es);
+                }
     }
     return ORC_OK;
 }

@@ -2,7 +2,8 @@
 source (a dropped token, a reversed offset, a transposed layout, a missing
 scale, a wrong sign, a wrong operand, a missing normalisation, a shifted
 index, a wrong exponent bias, swapped block/offset, half a copy, mirrored
-heads) each make at least one pin of tests/test_oracle_pins.py fail.  The
+heads, and in the swap: only K, a missed offset, mirrored heads, only the
+first pair) each make at least one pin of tests/test_oracle_pins.py fail.  The
 mutants are built in a temporary directory on the CPU; oracle/oracle.c is
 never changed.  No GPU."""
 import os
@@ -38,6 +39,13 @@ MUTATIONS = {
                     ";"),
     "mirrored-heads-in-write": ("const int64_t src = ((int64_t)i * H + h) * D;",
                                 "const int64_t src = ((int64_t)i * H + (H - 1 - h)) * D;"),
+    "swap-k-only": ("memcpy((char *)dst_v + to * es, (const char *)src_v + from * es, es);", ";"),
+    "swap-misses-last-offset": ("            for (int o = 0; o < B; ++o)\n                for (int d = 0; d < D; ++d) {\n                    const int64_t from",
+                                "            for (int o = 0; o < B - 1; ++o)\n                for (int d = 0; d < D; ++d) {\n                    const int64_t from"),
+    "swap-mirrored-heads": ("const int64_t from = pool_index(src, h, o, d, H, B, D);",
+                            "const int64_t from = pool_index(src, H - 1 - h, o, d, H, B, D);"),
+    "swap-first-pair-only": ("    for (int i = 0; i < num_pairs; ++i) {\n        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];\n        for (int h",
+                             "    for (int i = 0; i < 1 && i < num_pairs; ++i) {\n        const int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];\n        for (int h"),
 }
 
 # The pins, each run against a mutant; any AssertionError or oracle error
@@ -56,6 +64,9 @@ PINS = {
     "step-cfg1": lambda o: pins.test_step_reproduces_placement(o, lambda: W.config1()),
     "write-read-back": lambda o: pins.test_write_then_read_back(o),
     "sharing-diagram": lambda o: pins.test_sharing_diagram(o),
+    "swap-round-trip": lambda o: pins.test_swap_round_trip_leaves_decode_unchanged(o),
+    "swap-block-slices": lambda o: pins.test_swap_equals_whole_block_slices(o),
+    "swap-is-copy-in-one-pool": lambda o: pins.test_swap_within_one_pool_is_copy_blocks(o),
 }
 
 

@@ -516,3 +516,95 @@ def test_split_merge_identity(oracle_lib, part):
             w = np.exp(np.array(ms) - M)
             merged = (w[:, None] * np.array(os_)).sum(0) / (w * np.array(ls)).sum()
             assert np.allclose(merged, ref[b, h], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# swapping (wywy.jp Keyword "Swapping", Overview scheduling and preemption;
+# zhaifeiyue "Scheduling & Preemption" table, row "Swap")
+# --------------------------------------------------------------------------
+
+def swap_workload(seed=12):
+    """Config-1 sequences with a host pool of another size to swap into."""
+    wl = W.config1(seed=seed)
+    NB = wl.num_blocks
+    nb = [-(-int(c) // wl.block_size) for c in wl.context_lens]
+    return wl, NB, nb
+
+
+def test_swap_round_trip_leaves_decode_unchanged(oracle_lib):
+    """Every block of every sequence goes to a host pool (other ids, other
+    pool size) and back to fresh device blocks; with the tables rewritten
+    the decode is exactly the one before (fp64, same order of sums), and the
+    host-pool decode with the host tables is too."""
+    wl, NB, nb = swap_workload()
+    before = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                               wl.scale)
+    rng = np.random.default_rng(5)
+    used = sorted({int(b) for r, n in zip(wl.block_tables, nb) for b in r[:n]})
+    HNB = len(used) + 3
+    host_ids = rng.permutation(HNB)[:len(used)]
+    to_host = dict(zip(used, host_ids.tolist()))
+    shape = (HNB,) + wl.k_pool.shape[1:]
+    hk = np.full(shape, np.nan, wl.k_pool.dtype)
+    hv = np.full(shape, np.nan, wl.v_pool.dtype)
+    oracle_lib.swap_blocks(hk, hv, wl.k_pool, wl.v_pool, [[b, to_host[b]] for b in used])
+    host_tables = wl.block_tables.copy()
+    for r, n in zip(host_tables, nb):
+        r[:n] = [to_host[int(b)] for b in r[:n]]
+    on_host = oracle_lib.decode(wl.q, hk, hv, host_tables, wl.context_lens, wl.scale)
+    assert np.array_equal(on_host, before)
+    # back in: to device blocks other than the ones they came from
+    free = [b for b in rng.permutation(NB).tolist()]
+    back = dict(zip(host_ids.tolist(), free[:len(used)]))
+    dk = np.full(wl.k_pool.shape, np.nan, wl.k_pool.dtype)
+    dv = np.full(wl.v_pool.shape, np.nan, wl.v_pool.dtype)
+    oracle_lib.swap_blocks(dk, dv, hk, hv, [[h, back[h]] for h in host_ids.tolist()])
+    dev_tables = host_tables.copy()
+    for r, n in zip(dev_tables, nb):
+        r[:n] = [back[int(b)] for b in r[:n]]
+    after = oracle_lib.decode(wl.q, dk, dv, dev_tables, wl.context_lens, wl.scale)
+    assert np.array_equal(after, before)
+
+
+def test_swap_equals_whole_block_slices(oracle_lib):
+    """Each destination block equals its source block bit for bit (numpy
+    whole-block indexing); every other destination block is untouched."""
+    rng = np.random.default_rng(8)
+    for dtype, (H, B, D) in ((np.float16, (3, 8, 64)), (np.float32, (2, 16, 32))):
+        sk = rng.standard_normal((9, H, B, D)).astype(dtype)
+        sv = rng.standard_normal((9, H, B, D)).astype(dtype)
+        dk = rng.standard_normal((5, H, B, D)).astype(dtype)
+        dv = rng.standard_normal((5, H, B, D)).astype(dtype)
+        pairs = np.array([[7, 2], [0, 4], [7, 0]])     # one source to two places
+        ek, ev = dk.copy(), dv.copy()
+        for s, d in pairs:
+            ek[d] = sk[s]
+            ev[d] = sv[s]
+        oracle_lib.swap_blocks(dk, dv, sk, sv, pairs)
+        view = np.uint16 if dtype == np.float16 else np.uint32
+        assert np.array_equal(dk.view(view), ek.view(view))
+        assert np.array_equal(dv.view(view), ev.view(view))
+
+
+def test_swap_within_one_pool_is_copy_blocks(oracle_lib):
+    """With the source pools as destination the swap is the copy-on-write
+    block copy (pinned by the worked example)."""
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((8, 2, 4, 16)).astype(np.float32)
+    v = rng.standard_normal((8, 2, 4, 16)).astype(np.float32)
+    pairs = np.array([[1, 3], [1, 6], [2, 0]])
+    k2, v2 = k.copy(), v.copy()
+    oracle_lib.copy_blocks(k2, v2, pairs)
+    oracle_lib.swap_blocks(k, v, k.copy(), v.copy(), pairs)
+    assert np.array_equal(k, k2) and np.array_equal(v, v2)
+
+
+def test_swap_rejects(oracle_lib):
+    src = np.zeros((6, 1, 4, 8), np.float32)
+    dst = np.zeros((3, 1, 4, 8), np.float32)
+    with pytest.raises(oracle_lib.OracleError):          # valid source, no such destination
+        oracle_lib.swap_blocks(dst, dst.copy(), src, src, [[5, 3]])
+    with pytest.raises(oracle_lib.OracleError):          # no such source
+        oracle_lib.swap_blocks(dst, dst.copy(), src, src, [[6, 0]])
+    with pytest.raises(oracle_lib.OracleError):          # one destination twice
+        oracle_lib.swap_blocks(dst, dst.copy(), src, src, [[0, 1], [2, 1]])
