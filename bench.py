@@ -21,6 +21,8 @@ threads) as a reported baseline, and checks sampled GPU rows against it.
 ``--workload generation`` instead times the multi-step decoding loop that
 the host block manager drives (parallel sampling with beam-like pruning at
 the same layer shape, every step over all L layers) and prints its own line.
+``--workload swap`` times block swapping between the device pool and a
+pinned host pool against the block size and prints its own line.
 """
 import argparse
 import hashlib
@@ -80,6 +82,112 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "torch.mul fp32 copy", "read_bytes": 4 * n,
                       "write_bytes": 4 * n}), flush=True)
+    return 0
+
+
+PCIE_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction, before protocol overhead
+
+
+def bench_swap(args):
+    """Swap of one OPT-13B-shaped layer's KV for 32768 tokens (40 heads x
+    head_dim 128, fp16, K and V: 671 MB each way) between the device pool and
+    a pinned host pool, blocks mapped at random, for block sizes 1..256:
+    pa_swap_blocks (one launch; the kernel moves the bytes over PCIe) against
+    one hipMemcpyAsync per block and pool (torch copy_ of pinned views: the
+    DMA path whose per-transfer cost grows with the number of blocks), with
+    one contiguous copy of the same bytes as the ceiling."""
+    import torch
+
+    import paged_kv_cache_05_amd as pa
+
+    device = torch.device("cuda:0")
+    H, D, T = 40, 128, 32768
+    es = 2
+    total = 2 * T * H * D * es                    # K and V bytes moved per direction
+    stream = torch.cuda.current_stream()
+    reps = max(1, min(args.steps, 5))
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
+
+    # ceiling: one contiguous copy each way
+    flat_d = torch.empty(total // 2, dtype=torch.float16, device=device)
+    flat_h = torch.empty(total // 2, dtype=torch.float16).pin_memory()
+    ceil_out = total / timed(lambda: flat_h.copy_(flat_d, non_blocking=True), reps) / 1e9
+    ceil_in = total / timed(lambda: flat_d.copy_(flat_h, non_blocking=True), reps) / 1e9
+    del flat_d, flat_h
+
+    rng = np.random.default_rng(31)
+    curve = {}
+    for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        NB = T // B
+        shape = (NB, H, B, D)
+        dk = torch.randn(shape, dtype=torch.float16, device=device)
+        dv = torch.randn(shape, dtype=torch.float16, device=device)
+        hk = torch.empty(shape, dtype=torch.float16).pin_memory()
+        hv = torch.empty(shape, dtype=torch.float16).pin_memory()
+        perm_d, perm_h = rng.permutation(NB), rng.permutation(NB)
+        out_pairs = torch.from_numpy(np.stack([perm_d, perm_h], 1).astype(np.int64)).to(device)
+        in_pairs = torch.from_numpy(np.stack([perm_h, perm_d], 1).astype(np.int64)).to(device)
+        k_out = timed(lambda: pa.pa_swap_blocks(hk, hv, dk, dv, out_pairs), reps)
+        k_in = timed(lambda: pa.pa_swap_blocks(dk, dv, hk, hv, in_pairs), reps)
+        # the round trip must give back the same bits
+        ref = dk[int(perm_d[0])].clone()
+        pa.pa_swap_blocks(hk, hv, dk, dv, out_pairs)
+        dk.zero_()
+        pa.pa_swap_blocks(dk, dv, hk, hv, in_pairs)
+        torch.cuda.synchronize()
+        if not torch.equal(dk[int(perm_d[0])], ref):
+            raise SystemExit(f"bench: swap round trip changed block bits at B={B}")
+        pd, ph = perm_d.tolist(), perm_h.tolist()
+
+        def dma_out():
+            for d_, h_ in zip(pd, ph):
+                hk[h_].copy_(dk[d_], non_blocking=True)
+                hv[h_].copy_(dv[d_], non_blocking=True)
+
+        def dma_in():
+            for d_, h_ in zip(pd, ph):
+                dk[d_].copy_(hk[h_], non_blocking=True)
+                dv[d_].copy_(hv[h_], non_blocking=True)
+
+        w0 = time.perf_counter()
+        d_out = timed(dma_out, 1)
+        d_in = timed(dma_in, 1)
+        curve[B] = {"blocks": NB, "block_bytes": H * B * D * es,
+                    "kernel_out_GBps": round(total / k_out / 1e9, 2),
+                    "kernel_in_GBps": round(total / k_in / 1e9, 2),
+                    "dma_per_block_out_GBps": round(total / d_out / 1e9, 2),
+                    "dma_per_block_in_GBps": round(total / d_in / 1e9, 2)}
+        print(f"# B={B}: {curve[B]} ({time.perf_counter() - w0:.1f} s of per-block copies)",
+              file=sys.stderr, flush=True)
+        del dk, dv, hk, hv
+        torch.cuda.empty_cache()
+    c16 = curve[16]
+    value = 2 * total / (total / (c16["kernel_out_GBps"] * 1e9) + total / (c16["kernel_in_GBps"] * 1e9)) / 1e9
+    rec = {
+        "metric": "KV block swap GB/s (device <-> pinned host, out and in), block size 16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(2 * total / (value * 1e9) * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (N(0,1) K/V, random block mapping)",
+        "config": {"workload": "swap one OPT-13B-shaped layer's KV of 32768 tokens out and in",
+                   "num_heads": H, "head_dim": D, "tokens": T, "bytes_each_way": total},
+        "roofline": {"bound": "pcie", "achieved": round(value, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "move_blocks_kernel"},
+        "contiguous_copy_GBps": {"out": round(ceil_out, 2), "in": round(ceil_in, 2)},
+        "curve_by_block_size": curve,
+    }
+    print(json.dumps(rec), flush=True)
     return 0
 
 
@@ -207,9 +315,10 @@ def main():
                     help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
-    ap.add_argument("--workload", choices=["decode", "generation"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "generation", "swap"], default="decode",
                     help="decode: one layer's decode step (the default line); generation: the "
-                         "block-manager decoding loop over all layers")
+                         "block-manager decoding loop over all layers; swap: block swap "
+                         "device <-> pinned host against the block size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus "
@@ -220,6 +329,8 @@ def main():
         return calibrate_copy()
     if args.workload == "generation":
         return bench_generation(args)
+    if args.workload == "swap":
+        return bench_swap(args)
 
     import torch
 

@@ -14,7 +14,9 @@
  * Conventions for every entry point
  * ---------------------------------
  *  - Every pointer argument is device memory owned by the caller (except
- *    `stream`, a hipStream_t, and the return of pa_status_string).  The
+ *    `stream`, a hipStream_t; the returns of pa_status_string and
+ *    pa_last_error; and the pools of pa_swap_blocks, which may also be
+ *    pinned host memory).  The
  *    library allocates nothing, frees nothing and keeps no state between
  *    calls apart from a per-thread error description (pa_last_error).  It
  *    is thread-safe.
@@ -189,6 +191,39 @@ int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,
 int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
                    int num_pairs, int num_heads, int head_dim, int block_size,
                    int num_blocks, int dtype, void *stream);
+
+/*
+ * Swapping: copy whole blocks between two pool pairs, typically the device
+ * pools and pinned host pools (swap out: device -> host; swap in: host ->
+ * device).  Source: the PagedAttention pages -- the wywy.jp notes, Keyword
+ * "Swapping" and "All-or-nothing eviction" and Overview, scheduling and
+ * preemption (every KV block of an evicted sequence is copied from GPU to
+ * CPU memory, and back whole when it resumes; the CPU swap space never
+ * needs more blocks than the GPU pool holds); the zhaifeiyue.github.io
+ * summary, "Scheduling & Preemption" table, row "Swap".
+ *
+ *   for each i: block block_mapping[2i] of (src_k, src_v) is copied onto
+ *   block block_mapping[2i+1] of (dst_k, dst_v), K and V, bit for bit.
+ *
+ * Pools: [src_num_blocks] (resp. [dst_num_blocks]) x [num_heads][block_size]
+ * [head_dim] of `dtype`, 16-byte aligned; both pairs have the same block
+ * shape.  Blocks move as bytes, so any positive geometry is accepted whose
+ * block span (num_heads * block_size * head_dim * element bytes) is a
+ * multiple of 16 bytes (PA_ERR_SHAPE otherwise).  Each of dst_k, dst_v, src_k, src_v and block_mapping (int64
+ * [num_pairs][2]) must be device memory or pinned host memory (hipHostMalloc,
+ * or torch's pin_memory) that the GPU reaches at the same address: the
+ * kernel moves the bytes itself, over PCIe for the host side, in one launch
+ * for any number of blocks.  Anything else -- pageable host memory, managed
+ * memory -- returns PA_ERR_UNSUPPORTED before any launch (pa_last_error
+ * names the pointer).  Destinations must be distinct and must not overlap
+ * any source; a pair outside either pool is skipped.  Asynchronous on
+ * `stream`: host memory written by a swap out is complete once the stream
+ * has been synchronised.
+ */
+int pa_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                   const int64_t *block_mapping, int num_pairs, int num_heads, int head_dim,
+                   int block_size, int src_num_blocks, int dst_num_blocks, int dtype,
+                   void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *pa_status_string(int status);

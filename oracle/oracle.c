@@ -52,8 +52,10 @@
  * 40-digit evaluation of the block-wise equation, closed forms (one token,
  * zero query, equal keys, two tokens, weights summing to one), invariance
  * under re-placement, block size and shared-versus-copied prefixes, the
- * pages' copy-on-write example and sharing diagram, and an append-process
- * simulation of the manager for the address translation.
+ * pages' copy-on-write example and sharing diagram, an append-process
+ * simulation of the manager for the address translation, and for the swap a
+ * round trip that leaves the decode unchanged, whole-block slices and its
+ * reduction to copy_blocks within one pool.
  */
 #include <math.h>
 #include <stdint.h>

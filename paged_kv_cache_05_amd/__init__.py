@@ -41,11 +41,12 @@ def default_partition(max_context_len: int) -> int:
 
 # Every symbol include/pa.h and include/pa_manager.h declare.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
-           "pa_copy_blocks", "pa_status_string", "pa_last_error",
+           "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_last_error",
            "pa_manager_create", "pa_manager_destroy", "pa_manager_add", "pa_manager_fork",
            "pa_manager_append", "pa_manager_free", "pa_manager_tables", "pa_manager_num_free",
            "pa_manager_num_sequences", "pa_manager_refcount", "pa_manager_length",
-           "pa_manager_check")
+           "pa_manager_check", "pa_manager_swap_out", "pa_manager_swap_in",
+           "pa_manager_num_free_host", "pa_manager_is_swapped")
 
 
 class PAError(RuntimeError):
@@ -94,6 +95,8 @@ def library() -> ctypes.CDLL:
     lib.pa_write_kv.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
@@ -248,3 +251,36 @@ def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
         _dev(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0], H, D, B, NB,
         _dtype_code(k_pool), _stream(stream))
     _check(rc, "pa_copy_blocks")
+
+
+def _reachable(t, name, dtype=None):
+    """Pointer of a device tensor or of a pinned host tensor."""
+    if not t.is_cuda and not t.is_pinned():
+        raise PAError(f"{name} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise PAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PAError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
+    """Copy block src of (src_k, src_v) onto block dst of (dst_k, dst_v) for
+    every (src, dst) = block_mapping[i] (int64 [P][2]).  Each tensor is a
+    device tensor or a pinned host tensor (swap out: device pools -> pinned
+    host pools; swap in: the reverse)."""
+    import torch
+    sNB, H, B, D = src_k.shape
+    dNB = dst_k.shape[0]
+    if (tuple(dst_k.shape[1:]) != (H, B, D) or tuple(src_v.shape) != tuple(src_k.shape)
+            or tuple(dst_v.shape) != tuple(dst_k.shape)):
+        raise PAError("pa_swap_blocks: pools differ in block shape")
+    if len({t.dtype for t in (dst_k, dst_v, src_k, src_v)}) != 1:
+        raise PAError("pa_swap_blocks: pools differ in element type")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise PAError("pa_swap_blocks: block_mapping must be [P][2]")
+    rc = library().pa_swap_blocks(
+        _reachable(dst_k, "dst_k"), _reachable(dst_v, "dst_v"), _reachable(src_k, "src_k"),
+        _reachable(src_v, "src_v"), _reachable(block_mapping, "block_mapping", torch.int64),
+        block_mapping.shape[0], H, D, B, sNB, dNB, _dtype_code(src_k), _stream(stream))
+    _check(rc, "pa_swap_blocks")

@@ -56,6 +56,30 @@ thread_local char t_detail[384] = "";
 // so a launch first takes whatever an earlier call (of the caller, or of a
 // framework around it) left behind; the status read after the launch then
 // belongs to the launch.  Both are described for pa_last_error.
+// True if the GPU can reach p at that address: device memory, or pinned
+// host memory mapped at the same address.  Pageable host memory (which a
+// kernel cannot touch without faulting) and managed memory are refused, and
+// the reason goes to pa_last_error.
+bool gpu_reachable(const void *p, const char *what) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the query's failure pending
+    snprintf(t_detail, sizeof t_detail,
+             "%s is not memory the HIP runtime knows (%s): pageable host memory is not "
+             "reachable by the GPU; use device or pinned host memory",
+             what, hipGetErrorName(e));
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice) return true;
+  if (a.type == hipMemoryTypeHost && a.devicePointer == p) return true;
+  snprintf(t_detail, sizeof t_detail,
+           "%s: memory type %d (device pointer %p for %p) is neither device memory nor pinned "
+           "host memory at the same address",
+           what, (int)a.type, a.devicePointer, p);
+  return false;
+}
+
 template <class Launch>
 int launch_checked(const char *what, Launch &&launch) {
   const hipError_t stale = hipGetLastError();
@@ -152,6 +176,36 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 
 extern "C" {
 
+int pa_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                   const int64_t *block_mapping, int num_pairs, int num_heads, int head_dim,
+                   int block_size, int src_num_blocks, int dst_num_blocks, int dtype,
+                   void *stream) {
+  // Whole blocks move as bytes: any geometry whose block span is a whole
+  // number of 16-byte chunks.
+  if (!elem_bytes(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_heads <= 0 || head_dim <= 0 || block_size <= 0 || src_num_blocks <= 0 ||
+      dst_num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  const int64_t span = (int64_t)num_heads * block_size * head_dim * elem_bytes(dtype);
+  if (span % 16 != 0 || span > ((int64_t)1 << 40)) return PA_ERR_SHAPE;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v) ||
+      ((uintptr_t)block_mapping & 7u))
+    return PA_ERR_SHAPE;
+  if (!gpu_reachable(dst_k, "dst_k") || !gpu_reachable(dst_v, "dst_v") ||
+      !gpu_reachable(src_k, "src_k") || !gpu_reachable(src_v, "src_v") ||
+      !gpu_reachable(block_mapping, "block_mapping"))
+    return PA_ERR_UNSUPPORTED;
+  const size_t block_bytes = (size_t)num_heads * block_size * head_dim * elem_bytes(dtype);
+  return launch_checked("pa_swap_blocks", [&] {
+    return pa::launch_move_blocks(dst_k, dst_v, src_k, src_v, block_mapping, num_pairs,
+                                  block_bytes, src_num_blocks, dst_num_blocks,
+                                  static_cast<hipStream_t>(stream));
+  });
+}
+
 const char *pa_last_error(void) { return t_detail; }
 
 const char *pa_status_string(int status) {
@@ -159,12 +213,14 @@ const char *pa_status_string(int status) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "a size is out of range or a pointer is misaligned";
-    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
+    case PA_ERR_UNSUPPORTED:
+      return "unsupported head_dim, block_size or dtype, or memory the GPU cannot reach";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error at launch";
     case PA_ERR_NO_SEQUENCE: return "no sequence with that id";
     case PA_ERR_EXISTS: return "a sequence with that id already exists";
     case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PA_ERR_SWAPPED: return "the sequence is swapped out";
   }
   return "unknown status";
 }

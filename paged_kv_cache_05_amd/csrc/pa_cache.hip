@@ -13,10 +13,18 @@
 //    the block engine copies the old one into it (wywy.jp WHERE, the
 //    parallel-sampling example with physical blocks 1 and 3; zhaifeiyue
 //    memory-management table, "Copy-on-Write").
+//  * swap_blocks: swapping moves every block of an evicted sequence from GPU
+//    memory to CPU memory and back whole when it resumes (wywy.jp Keyword
+//    "Swapping" and Overview, scheduling and preemption; zhaifeiyue
+//    "Scheduling & Preemption" table, row "Swap").  The host pools are
+//    pinned memory the GPU reaches directly, so the kernel itself moves the
+//    bytes over PCIe: one launch for any number of blocks, instead of one
+//    DMA transfer per block (the pages note that small blocks make swapping
+//    slow through many small CPU-GPU transfers).
 //
 // With the [num_blocks][num_heads][block_size][head_dim] pool layout a whole
 // block is one contiguous span, and a token row of one head is one contiguous
-// row_bytes span, so both kernels are streams of aligned 16-byte moves.
+// row_bytes span, so all kernels are streams of aligned 16-byte moves.
 #include "pa_kernels.h"
 
 namespace pa {
@@ -46,21 +54,41 @@ write_kv_kernel(const uint4 *__restrict__ key, const uint4 *__restrict__ value,
   v_pool[dst] = value[i];
 }
 
-// grid.x = copy pair, grid.y strides over the block's chunks.
+// grid.x = block pair, grid.y strides over the block's 16-byte chunks.
+// Copies block src of (src_k, src_v) onto block dst of (dst_k, dst_v); the
+// copy-on-write copy passes the same pools on both sides.  Each thread keeps
+// kUnroll chunks of K and of V in flight before storing them, which hides the
+// latency of reads from host memory over PCIe.
+constexpr int kUnroll = 4;
+
 __global__ void __launch_bounds__(kThreads)
-copy_blocks_kernel(uint4 *__restrict__ k_pool, uint4 *__restrict__ v_pool,
+move_blocks_kernel(uint4 *dst_k, uint4 *dst_v, const uint4 *src_k, const uint4 *src_v,
                    const int64_t *__restrict__ block_mapping, int64_t chunks_per_block,
-                   int64_t num_blocks) {
+                   int64_t src_blocks, int64_t dst_blocks) {
   const int64_t pair = blockIdx.x;
   const int64_t src = block_mapping[2 * pair];
   const int64_t dst = block_mapping[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const uint4 *ks = k_pool + src * chunks_per_block;
-  const uint4 *vs = v_pool + src * chunks_per_block;
-  uint4 *kd = k_pool + dst * chunks_per_block;
-  uint4 *vd = v_pool + dst * chunks_per_block;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4 *ks = src_k + src * chunks_per_block;
+  const uint4 *vs = src_v + src * chunks_per_block;
+  uint4 *kd = dst_k + dst * chunks_per_block;
+  uint4 *vd = dst_v + dst * chunks_per_block;
   const int64_t stride = (int64_t)gridDim.y * kThreads;
-  for (int64_t c = (int64_t)blockIdx.y * kThreads + threadIdx.x; c < chunks_per_block; c += stride) {
+  int64_t c = (int64_t)blockIdx.y * kThreads + threadIdx.x;
+  for (; c + (kUnroll - 1) * stride < chunks_per_block; c += kUnroll * stride) {
+    uint4 a[kUnroll], b[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      a[u] = ks[c + u * stride];
+      b[u] = vs[c + u * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      kd[c + u * stride] = a[u];
+      vd[c + u * stride] = b[u];
+    }
+  }
+  for (; c < chunks_per_block; c += stride) {
     const uint4 a = ks[c];
     const uint4 b = vs[c];
     kd[c] = a;
@@ -84,16 +112,24 @@ hipError_t launch_write_kv(const void *key, const void *value, void *k_pool, voi
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
-                              int num_pairs, size_t block_bytes, int num_blocks,
-                              hipStream_t stream) {
+hipError_t launch_move_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                              const int64_t *block_mapping, int num_pairs, size_t block_bytes,
+                              int src_blocks, int dst_blocks, hipStream_t stream) {
   const int64_t chunks = (int64_t)(block_bytes / 16);
   int64_t ys = (chunks + kThreads - 1) / kThreads;
   if (ys > 64) ys = 64;  // each thread then copies several chunks
-  copy_blocks_kernel<<<dim3((unsigned)num_pairs, (unsigned)ys), kThreads, 0, stream>>>(
-      static_cast<uint4 *>(k_pool), static_cast<uint4 *>(v_pool), block_mapping, chunks,
-      (int64_t)num_blocks);
+  move_blocks_kernel<<<dim3((unsigned)num_pairs, (unsigned)ys), kThreads, 0, stream>>>(
+      static_cast<uint4 *>(dst_k), static_cast<uint4 *>(dst_v),
+      static_cast<const uint4 *>(src_k), static_cast<const uint4 *>(src_v), block_mapping,
+      chunks, (int64_t)src_blocks, (int64_t)dst_blocks);
   return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
+                              int num_pairs, size_t block_bytes, int num_blocks,
+                              hipStream_t stream) {
+  return launch_move_blocks(k_pool, v_pool, k_pool, v_pool, block_mapping, num_pairs,
+                            block_bytes, num_blocks, num_blocks, stream);
 }
 
 }  // namespace pa

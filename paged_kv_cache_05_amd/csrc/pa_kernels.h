@@ -59,4 +59,10 @@ hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_m
                               int num_pairs, size_t block_bytes, int num_blocks,
                               hipStream_t stream);
 
+// Block src of (src_k, src_v) onto block dst of (dst_k, dst_v), per pair;
+// either side may be pinned host memory the GPU reaches at that address.
+hipError_t launch_move_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                              const int64_t *block_mapping, int num_pairs, size_t block_bytes,
+                              int src_blocks, int dst_blocks, hipStream_t stream);
+
 }  // namespace pa

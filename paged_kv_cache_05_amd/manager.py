@@ -18,11 +18,12 @@ import time
 import numpy as np
 
 from . import PAError, library, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, \
-    pa_status_string, pa_write_kv
+    pa_status_string, pa_swap_blocks, pa_write_kv
 
 PA_ERR_NO_SEQUENCE = -6
 PA_ERR_EXISTS = -7
 PA_ERR_NO_BLOCKS = -8
+PA_ERR_SWAPPED = -9
 
 
 class OutOfBlocks(PAError):
@@ -33,7 +34,7 @@ def _bind(lib):
     if getattr(lib, "_pa_manager_bound", False):
         return lib
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
-    lib.pa_manager_create.argtypes = [i32, i32, vp]
+    lib.pa_manager_create.argtypes = [i32, i32, i32, vp]
     lib.pa_manager_create.restype = vp
     lib.pa_manager_destroy.argtypes = [vp]
     lib.pa_manager_destroy.restype = None
@@ -47,8 +48,13 @@ def _bind(lib):
     lib.pa_manager_refcount.argtypes = [vp, i32]
     lib.pa_manager_length.argtypes = [vp, i64]
     lib.pa_manager_check.argtypes = [vp]
+    lib.pa_manager_swap_out.argtypes = [vp, vp, i32, vp, i32, vp]
+    lib.pa_manager_swap_in.argtypes = [vp, vp, i32, vp, i32, vp]
+    lib.pa_manager_num_free_host.argtypes = [vp]
+    lib.pa_manager_is_swapped.argtypes = [vp, i64]
     for f in ("add", "fork", "append", "free", "tables", "num_free", "num_sequences",
-              "refcount", "length", "check"):
+              "refcount", "length", "check", "swap_out", "swap_in", "num_free_host",
+              "is_swapped"):
         getattr(lib, "pa_manager_" + f).restype = i32
     lib._pa_manager_bound = True
     return lib
@@ -63,20 +69,23 @@ def _check(rc, what):
 
 
 class BlockManager:
-    """Physical blocks 0..num_blocks-1 of block_size tokens (host state).
+    """GPU blocks 0..num_blocks-1 of block_size tokens and a CPU swap space
+    of num_host_blocks blocks (host state only).
 
     ``lib`` is the ctypes library exporting the ``pa_manager_*`` functions
     (default: this package's libpa.so)."""
 
-    def __init__(self, num_blocks, block_size, alloc_order=None, lib=None):
+    def __init__(self, num_blocks, block_size, alloc_order=None, num_host_blocks=0, lib=None):
         self._lib = _bind(lib if lib is not None else library())
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.num_host_blocks = int(num_host_blocks)
         order = None
         if alloc_order is not None:
             order = np.ascontiguousarray(alloc_order, dtype=np.int32)
             if order.shape != (self.num_blocks,):
                 raise PAError("alloc_order must list every block once")
         self._h = self._lib.pa_manager_create(self.num_blocks, self.block_size,
+                                              self.num_host_blocks,
                                               None if order is None else order.ctypes.data)
         if not self._h:
             raise PAError("pa_manager_create: bad arguments")
@@ -107,6 +116,30 @@ class BlockManager:
                                            pairs.ctypes.data, pairs.shape[0],
                                            ctypes.byref(npairs)), "append")
         return slots, pairs[:npairs.value].copy()
+
+    def _move(self, fn, seqs, what):
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        cap = max(self.num_blocks, self.num_host_blocks, 1)
+        pairs = np.empty((cap, 2), dtype=np.int64)
+        npairs = ctypes.c_int(0)
+        _check(fn(self._h, ids.ctypes.data, len(ids), pairs.ctypes.data, cap,
+                  ctypes.byref(npairs)), what)
+        return pairs[:npairs.value].copy()
+
+    def swap_out(self, seqs):
+        """Evict a group of sequences to the swap space: (gpu, host) pairs."""
+        return self._move(self._lib.pa_manager_swap_out, seqs, "swap_out")
+
+    def swap_in(self, seqs):
+        """Bring a swapped-out group back: (host, gpu) pairs."""
+        return self._move(self._lib.pa_manager_swap_in, seqs, "swap_in")
+
+    @property
+    def num_free_host(self):
+        return _check(self._lib.pa_manager_num_free_host(self._h), "num_free_host")
+
+    def is_swapped(self, seq):
+        return bool(_check(self._lib.pa_manager_is_swapped(self._h, int(seq)), "is_swapped"))
 
     def tables(self, seqs, max_blocks):
         """Block tables (int32 [n][max_blocks], -1 padded) and context lengths."""
@@ -151,20 +184,38 @@ class DecodeStepper:
     single BlockManager manages (every layer of a model shares the block
     tables; only the pool contents differ).
 
-    ``pools`` is one (k_pool, v_pool) pair or a list of them, one per layer.
-    :meth:`plan` makes the step's host decisions and uploads them with one
-    host-to-device copy from pinned memory; :meth:`layer` runs the step's
-    device work on one layer: copy-on-write copies (pa_copy_blocks), the
-    new token's K/V (pa_write_kv), decode attention (pa_decode).  All device
-    work goes to torch's current stream.
+    ``pools`` is one (k_pool, v_pool) pair or a list of them, one per layer;
+    ``host_pools`` (optional, same form, pinned host tensors of
+    manager.num_host_blocks blocks) is the swap space.  :meth:`plan` makes
+    the step's host decisions and uploads them with one host-to-device copy
+    from pinned memory; :meth:`layer` runs the step's device work on one
+    layer: copy-on-write copies (pa_copy_blocks), the new token's K/V
+    (pa_write_kv), decode attention (pa_decode).  :meth:`swap_out` and
+    :meth:`swap_in` move a preempted group's blocks to the swap space and
+    back, on every layer (pa_swap_blocks).  All device work goes to torch's
+    current stream, so a swap-out's copies finish before the freed blocks
+    are written again.
     """
 
-    def __init__(self, manager: BlockManager, pools, max_blocks, partition_size=0):
+    def __init__(self, manager: BlockManager, pools, max_blocks, partition_size=0,
+                 host_pools=None):
         import torch
         self._torch = torch
-        if isinstance(pools, tuple) and len(pools) == 2 and hasattr(pools[0], "shape"):
-            pools = [pools]
-        self.pools = list(pools)
+
+        def as_list(p):
+            if isinstance(p, tuple) and len(p) == 2 and hasattr(p[0], "shape"):
+                return [p]
+            return list(p)
+
+        self.pools = as_list(pools)
+        self.host_pools = as_list(host_pools) if host_pools is not None else None
+        if self.host_pools is not None:
+            if len(self.host_pools) != len(self.pools):
+                raise PAError("one host pool pair per layer")
+            for (k, v), (hk, hv) in zip(self.pools, self.host_pools):
+                if (hk.shape[0] != manager.num_host_blocks or hk.shape[1:] != k.shape[1:]
+                        or hv.shape != hk.shape or hk.dtype != k.dtype or hv.dtype != k.dtype):
+                    raise PAError("host pools do not match the manager and the device pools")
         self.manager = manager
         self.max_blocks, self.partition_size = int(max_blocks), int(partition_size)
         self.device = self.pools[0][0].device
@@ -211,8 +262,9 @@ class DecodeStepper:
         return [dbuf[o:o + a.nbytes].view(tdt[a.dtype]).view(a.shape) for a, o in zip(arrays, offs)]
 
     def _workspace(self, n, H, D, maxctx):
-        # enough for the smallest partition the host-planned launch picks
-        need = pa_decode_workspace_bytes(n, H, D, maxctx, 256)
+        # an explicit partition size, or else the smallest partition the
+        # host-planned launch picks (256 tokens; it never needs more)
+        need = pa_decode_workspace_bytes(n, H, D, maxctx, self.partition_size or 256)
         if self._ws is None or self._ws.numel() < need:
             self._ws = self._torch.empty(max(need, 256), dtype=self._torch.uint8,
                                          device=self.device)
@@ -245,6 +297,28 @@ class DecodeStepper:
         pa_decode(out, q, k, v, plan.d_tables, plan.d_context_lens, scale, plan.max_context_len,
                   self.partition_size, ws, host_context_lens=plan.context_lens)
         return out
+
+    def _swap(self, pairs, out):
+        if self.host_pools is None:
+            raise PAError("no swap space: pass host_pools")
+        if len(pairs):
+            (d_pairs,) = self._upload([pairs])
+            for (k, v), (hk, hv) in zip(self.pools, self.host_pools):
+                if out:
+                    pa_swap_blocks(hk, hv, k, v, d_pairs)
+                else:
+                    pa_swap_blocks(k, v, hk, hv, d_pairs)
+        return pairs
+
+    def swap_out(self, seqs):
+        """Preempt a group: its blocks go to the swap space on every layer.
+        Returns the (gpu, host) pairs."""
+        return self._swap(self.manager.swap_out(seqs), True)
+
+    def swap_in(self, seqs):
+        """Resume a swapped-out group on fresh GPU blocks, every layer.
+        Returns the (host, gpu) pairs."""
+        return self._swap(self.manager.swap_in(seqs), False)
 
     def step(self, seqs, new_key, new_value, q, scale, out=None):
         """One step on the first (or only) layer: append one token

@@ -48,7 +48,7 @@ def test_header_constants_match_binding(pa):
 
 
 def test_status_strings(pa):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = pa.pa_status_string(code)
         assert s and s != "unknown status"
     assert pa.pa_status_string(-99) == "unknown status"
@@ -180,6 +180,21 @@ def test_write_and_copy_reject(pa):
     assert c(block_mapping=None) == -1 and c(v_pool=None) == -1
     assert c(head_dim=100) == -3 and c(num_pairs=-2) == -2 and c(k_pool=KP + 8) == -2
     assert c(num_pairs=0, block_mapping=None) == 0
+
+    oks = dict(dst_k=KP, dst_v=VP, src_k=Q, src_v=OUT, block_mapping=TB, num_pairs=3,
+               num_heads=2, head_dim=64, block_size=16, src_num_blocks=32, dst_num_blocks=8,
+               dtype=0, stream=None)
+
+    def sw(**o):
+        a = dict(oks)
+        a.update(o)
+        return lib.pa_swap_blocks(*a.values())
+
+    assert sw(dst_k=None) == -1 and sw(block_mapping=None) == -1
+    assert sw(dtype=7) == -3 and sw(num_pairs=-1) == -2 and sw(dst_num_blocks=0) == -2
+    assert sw(num_heads=1, head_dim=3, block_size=1) == -2     # 6-byte blocks
+    assert sw(src_k=Q + 8) == -2 and sw(block_mapping=TB + 4) == -2
+    assert sw(num_pairs=0, dst_k=None) == 0
 
 
 def test_one_hip_runtime_whatever_the_import_order():

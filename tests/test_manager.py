@@ -155,17 +155,93 @@ def test_parallel_sampling_saves_memory(M):
     m.check()
 
 
+def test_swap_out_and_in_keep_sharing(M):
+    """A group (prompt + 2 samples) is evicted whole: each distinct block
+    it holds goes to the swap space once, its GPU blocks are freed, and it
+    comes back with its sharing intact (wywy.jp Keyword "Swapping",
+    "All-or-nothing eviction")."""
+    B = 4
+    m = M.BlockManager(16, B, num_host_blocks=16)
+    m.add(0)
+    m.append([0] * 10)                  # blocks 0, 1 full; 2 holds 2 tokens
+    m.fork(0, 1)
+    m.fork(0, 2)
+    m.append([0, 1, 2])                 # 0 and 1 copy block 2; 2 writes in place
+    tables, _ = m.tables([0, 1, 2], 4)
+    distinct = {int(b) for b in tables[:, :3].ravel()}
+    assert len(distinct) == 5           # 2 shared + 3 private last blocks
+    free_before = m.num_free
+    pairs = m.swap_out([0, 1, 2])
+    assert len(pairs) == 5 and {int(a) for a, _ in pairs} == distinct
+    assert len({int(b) for _, b in pairs}) == 5
+    assert m.num_free == free_before + 5 and m.num_free_host == 16 - 5
+    assert all(m.is_swapped(s) for s in (0, 1, 2))
+    for call in (lambda: m.append([1]), lambda: m.tables([1], 4), lambda: m.fork(1, 9),
+                 lambda: m.swap_out([1])):
+        with pytest.raises(M.PAError):
+            call()
+    back = m.swap_in([2, 0, 1])
+    assert len(back) == 5 and sorted(int(a) for a, _ in back) == sorted(int(b) for _, b in pairs)
+    tables2, ctx = m.tables([0, 1, 2], 4)
+    assert ctx.tolist() == [11, 11, 11]
+    assert tables2[0, 0] == tables2[1, 0] == tables2[2, 0]       # still shared
+    assert tables2[0, 1] == tables2[1, 1] == tables2[2, 1]
+    assert len({int(x) for x in tables2[:, 2]}) == 3
+    assert m.refcount(int(tables2[0, 0])) == 3 and m.num_free_host == 16
+    m.check()
+
+
+def test_swap_out_part_of_a_group(M):
+    """Swapping out one of two sequences that share a block leaves the block
+    on the GPU for the other; the swapped one keeps a host copy."""
+    m = M.BlockManager(8, 4, num_host_blocks=8)
+    m.add(0)
+    m.append([0] * 8)                   # two full blocks
+    m.fork(0, 1)
+    pairs = m.swap_out([1])
+    assert len(pairs) == 2
+    assert m.refcount(0) == 1 and m.refcount(1) == 1 and m.num_free == 6
+    m.free(1)                           # a swapped sequence frees host blocks
+    assert m.num_free_host == 8
+    m.check()
+
+
+def test_swap_is_all_or_nothing(M):
+    m = M.BlockManager(8, 4, num_host_blocks=2)
+    m.add(0)
+    m.append([0] * 12)                  # three blocks
+    with pytest.raises(M.OutOfBlocks):
+        m.swap_out([0])                 # the swap space holds two
+    assert not m.is_swapped(0) and m.num_free == 5 and m.num_free_host == 2
+    m2 = M.BlockManager(4, 4, num_host_blocks=4)
+    for s in (0, 1):
+        m2.add(s)
+        m2.append([s] * 8)
+    m2.swap_out([1])
+    m2.add(2)
+    m2.append([2] * 5)                  # takes both freed blocks
+    with pytest.raises(M.OutOfBlocks):
+        m2.swap_in([1])
+    assert m2.is_swapped(1) and m2.num_free_host == 2
+    m2.free(2)
+    assert len(m2.swap_in([1])) == 2
+    m2.check()
+
+
 @st.composite
 def programs(draw):
     ops = []
     live = []
     next_id = 0
     for _ in range(draw(st.integers(5, 40))):
-        kind = draw(st.sampled_from(["add", "append", "append", "fork", "free"]))
+        kind = draw(st.sampled_from(["add", "append", "append", "fork", "free", "swap"]))
         if kind == "add" or not live:
             ops.append(("add", next_id))
             live.append(next_id)
             next_id += 1
+        elif kind == "swap":
+            k = draw(st.integers(1, min(3, len(live))))
+            ops.append(("swap", draw(st.permutations(live))[:k]))
         elif kind == "append":
             k = draw(st.integers(1, 6))
             ops.append(("append", [draw(st.sampled_from(live)) for _ in range(k)]))
@@ -182,11 +258,40 @@ def programs(draw):
 
 @settings(max_examples=150, deadline=None, derandomize=True,
           suppress_health_check=[HealthCheck.function_scoped_fixture])
-@given(programs(), st.sampled_from([1, 2, 4, 16]), st.integers(4, 40))
-def test_random_programs_keep_invariants(M, ops, B, nb):
-    m = M.BlockManager(nb, B)
+@given(programs(), st.sampled_from([1, 2, 4, 16]), st.integers(4, 40), st.integers(0, 40))
+def test_random_programs_keep_invariants(M, ops, B, nb, hnb):
+    """Random add / fork / append / free / swap programs.  A "swap" op
+    swaps its sequences out if all are resident, in if all are out."""
+    m = M.BlockManager(nb, B, num_host_blocks=hnb)
     lengths = {}
     for op in ops:
+        # ids named by ops that failed earlier (a fork of a swapped-out
+        # sequence) do not exist: skip what names them
+        named = op[1] if op[0] in ("append", "swap") else [op[1]]
+        if op[0] != "add" and any(i not in lengths for i in named):
+            continue
+        if op[0] == "swap":
+            state = {m.is_swapped(i) for i in op[1]}
+            if len(state) != 1:
+                continue
+            fn = m.swap_in if state.pop() else m.swap_out
+            free = (m.num_free, m.num_free_host)
+            try:
+                pairs = fn(op[1])
+            except M.OutOfBlocks:
+                assert (m.num_free, m.num_free_host) == free
+                continue
+            assert len({int(b) for _, b in pairs}) == len(pairs)
+            m.check()
+            continue
+        if op[0] == "append" and any(m.is_swapped(i) for i in op[1]):
+            with pytest.raises(M.PAError):
+                m.append(op[1])
+            continue
+        if op[0] == "fork" and m.is_swapped(op[1]):
+            with pytest.raises(M.PAError):
+                m.fork(op[1], op[2])
+            continue
         if op[0] == "add":
             m.add(op[1])
             lengths[op[1]] = 0
@@ -216,7 +321,7 @@ def test_random_programs_keep_invariants(M, ops, B, nb):
             for src, dst in pairs:
                 assert src != dst
         m.check()
-        ids = sorted(lengths)
+        ids = sorted(s for s in lengths if not m.is_swapped(s))
         if ids:
             tables, ctx = m.tables(ids, max(1, max(-(-lengths[i] // B) for i in ids)))
             assert ctx.tolist() == [lengths[i] for i in ids]
@@ -226,4 +331,5 @@ def test_random_programs_keep_invariants(M, ops, B, nb):
                 for b in row[:-(-lengths[i] // B)]:
                     held[int(b)] = held.get(int(b), 0) + 1
             assert all(m.refcount(b) == c for b, c in held.items())
+            # swapped-out sequences hold host blocks only
             assert m.num_free == nb - len(held)

@@ -566,3 +566,71 @@ def generation(seed=11, dtype=F16, num_heads=4, head_dim=128, block_size=16,
                       block_size=B, num_blocks=peak_blocks + P + 4,
                       max_blocks=_blocks_for(max_len, B), scale=np.float32(1.0 / math.sqrt(D)),
                       prompt_keys=prompt_keys, prompt_values=prompt_values, steps=out)
+
+
+# ---------------------------------------------------------------------------
+# Generation under memory pressure: groups of parallel samples that outgrow
+# the GPU pool, so that some group must be preempted (and swapped out) for
+# others to go on.  Inputs are keyed by (sequence, token index), not by step,
+# so a run that preempts and a run that does not feed every sequence the same
+# tokens.
+# ---------------------------------------------------------------------------
+
+def token_inputs(seed, seq, t, num_heads, head_dim, dtype):
+    """(key, value, q), [H][D] each, of generated token t of sequence seq."""
+    r = np.random.default_rng([int(seed), int(seq), int(t)])
+    dt = NP_DTYPES[dtype]
+    return tuple(_normal(r, (num_heads, head_dim), dt) for _ in range(3))
+
+
+@dataclass
+class Pressure:
+    name: str
+    seed: int
+    dtype: str
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int                 # GPU pool: too small for every group at once
+    num_host_blocks: int            # swap space: as many blocks as the GPU pool
+    max_blocks: int
+    scale: np.float32
+    groups: list                    # per group (arrival order), its sequence ids; the first is the prompt's
+    gen_lens: dict                  # sequence id -> tokens it generates
+    prompt_keys: list               # per group, [L][H][D]
+    prompt_values: list
+
+
+def pressure(seed=13, dtype=F16, num_heads=4, head_dim=64, block_size=16,
+             prompt_lens=(40, 70, 25, 90, 33), samples=3, gen=(20, 60), squeeze=0.55):
+    """Groups of `samples` sequences forked from one prompt each generate a
+    uniform [gen] number of tokens.  The GPU pool holds `squeeze` times the
+    blocks every group would need at its longest, but never less than one
+    group's worst case plus one block (so the earliest group can always
+    finish).  The swap space has as many blocks as the GPU pool (the pages'
+    bound on CPU swap space)."""
+    rng = np.random.default_rng(seed)
+    dt = NP_DTYPES[dtype]
+    H, D, B = num_heads, head_dim, block_size
+    groups, gen_lens, pk, pv = [], {}, [], []
+    sid = 0
+    need_all, need_max = 0, 0
+    for L in prompt_lens:
+        ids = list(range(sid, sid + samples))
+        sid += samples
+        groups.append(ids)
+        pk.append(_normal(rng, (int(L), H, D), dt))
+        pv.append(_normal(rng, (int(L), H, D), dt))
+        lens = [int(x) for x in rng.integers(gen[0], gen[1] + 1, size=samples)]
+        gen_lens.update(zip(ids, lens))
+        # the prompt's full blocks stay shared; each sample ends up with
+        # private blocks from the prompt's partial block on
+        need = int(L) // B + sum(_blocks_for(int(L) + n, B) - int(L) // B for n in lens)
+        need_all += need
+        need_max = max(need_max, need)
+    num_blocks = max(int(squeeze * need_all), need_max + 1)
+    max_len = max(prompt_lens) + gen[1]
+    return Pressure(name="pressure", seed=seed, dtype=dtype, num_heads=H, head_dim=D,
+                    block_size=B, num_blocks=num_blocks, num_host_blocks=num_blocks,
+                    max_blocks=_blocks_for(max_len, B), scale=np.float32(1.0 / math.sqrt(D)),
+                    groups=groups, gen_lens=gen_lens, prompt_keys=pk, prompt_values=pv)
