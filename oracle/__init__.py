@@ -16,6 +16,9 @@ What each function follows on the pages (Kwon et al., PagedAttention):
   "KV cache manager" (next free position of the last block).
 * :func:`copy_blocks` -- wywy.jp WHERE, parallel-sampling copy-on-write
   example; zhaifeiyue memory-management table, "Copy-on-Write".
+* :func:`prefill` -- wywy.jp Keyword "prompt phase" and WHERE, shared prefix
+  (a cached prefix's KV is reused; only the new tokens are queries); each
+  query attends causally over the context up to its own position.
 * :func:`swap_blocks` -- wywy.jp Keyword "Swapping" and Overview,
   scheduling and preemption (every block of an evicted sequence goes to CPU
   memory and comes back whole); zhaifeiyue "Scheduling & Preemption" table,
@@ -69,6 +72,9 @@ def _bind(lib):
     lib.oracle_write_kv.restype = i32
     lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
     lib.oracle_copy_blocks.restype = i32
+    lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   f32, i32, i32]
+    lib.oracle_prefill.restype = i32
     lib.oracle_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
     lib.oracle_swap_blocks.restype = i32
     lib.oracle_threads_available.argtypes = []
@@ -188,6 +194,40 @@ def copy_blocks(k_pool, v_pool, block_mapping, _lib_=None):
     _check(rc, "oracle copy_blocks")
 
 
+def prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, *, threads=0,
+            _lib_=None):
+    """fp64 paged prefill attention (causal).
+
+    q: [T][H][D] query rows of all sequences back to back; query_start: int
+    [N+1] row offsets; sequence b's rows are the last query_start[b+1] -
+    query_start[b] tokens of its context_lens[b]-token context.  Returns
+    float64 [T][H][D].
+    """
+    q = np.ascontiguousarray(q)
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    dt = _dtype_code(q)
+    if _dtype_code(k_pool) != dt or _dtype_code(v_pool) != dt:
+        raise OracleError("q, k_pool and v_pool must share one element type")
+    T, H, D = q.shape
+    NB, H2, B, D2 = k_pool.shape
+    N = ctx.shape[0]
+    if (H2, D2) != (H, D) or v_pool.shape != k_pool.shape:
+        raise OracleError("pool shape does not match q")
+    if qs.shape != (N + 1,) or int(qs[-1]) != T or tables.shape[0] != N:
+        raise OracleError("query_start / block_tables do not match the batch")
+    MB = tables.shape[1] if tables.ndim == 2 else 0
+    out = np.full((T, H, D), np.nan, dtype=np.float64)
+    rc = (_lib_ or _load()).oracle_prefill(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                           _ptr(tables), _ptr(ctx), _ptr(qs), N, H, D, B, NB,
+                                           MB, float(np.float32(scale)), dt, int(threads))
+    _check(rc, "oracle prefill")
+    return out
+
+
 def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, _lib_=None):
     """Copy block src of the source pools onto block dst of the destination
     pools for every (src, dst) pair, K and V (swap out or in)."""
@@ -232,6 +272,9 @@ class Oracle:
 
     def swap_blocks(self, *args):
         return swap_blocks(*args, _lib_=self._lib)
+
+    def prefill(self, *args, **kw):
+        return prefill(*args, _lib_=self._lib, **kw)
 
     def threads_available(self):
         return threads_available(_lib_=self._lib)

@@ -28,6 +28,13 @@
  *    physical block's contents into a newly allocated one (wywy.jp, WHERE,
  *    parallel-sampling example with physical blocks 1 and 3; zhaifeiyue,
  *    memory-management table, "Copy-on-Write"; ricepunchb section 5.1).
+ *  - prefill: the prompt phase, where every prompt token is known and all of
+ *    them are processed together (wywy.jp Keyword "prompt phase"; the shared
+ *    prefix of WHERE, whose cached KV is reused so that only the
+ *    request-specific tokens are computed).  The queries of a sequence are
+ *    the last tokens of its context; the query at position p attends
+ *    causally to tokens 0..p, that is, it is the decode above over the
+ *    context truncated to p + 1 tokens.
  *  - swap_blocks: swapping, the recovery that moves every KV block of an
  *    evicted sequence from GPU memory to CPU memory and back whole when it
  *    resumes (wywy.jp, Keyword "Swapping" and "All-or-nothing eviction",
@@ -260,6 +267,59 @@ int oracle_decode(double *out, const void *q, const void *k_pool, const void *v_
         const int rc = decode_one(out + ((int64_t)b * H + h) * D, w, q, k_pool, v_pool,
                                   block_tables, context_lens, b, h, H, D, B, NB, MB,
                                   (double)scale, dtype);
+        if (rc != ORC_OK) {
+#ifdef _OPENMP
+#pragma omp critical
+#endif
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/*
+ * Prefill: sequence b has context_lens[b] = n tokens in the pools, of which
+ * the last m = query_start[b+1] - query_start[b] are queries, in rows
+ * query_start[b] .. query_start[b+1]-1 of q and out ([T][H][D]).  Query i
+ * of the chunk is the token at position p = n - m + i; its output is the
+ * attention of its q row over tokens 0..p of the sequence.  query_start must
+ * start at 0, not decrease, and give every sequence m <= n.
+ */
+int oracle_prefill(double *out, const void *q, const void *k_pool, const void *v_pool,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start, int N, int H, int D, int B, int NB, int MB,
+                   float scale, int dtype, int threads)
+{
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+        return ORC_BAD_ARG;
+    if (N < 0 || H <= 0 || D <= 0 || B <= 0 || NB < 0 || MB < 0 || !elem_bytes(dtype))
+        return ORC_BAD_ARG;
+    if (query_start[0] != 0)
+        return ORC_BAD_ARG;
+    for (int b = 0; b < N; ++b) {
+        const int m = query_start[b + 1] - query_start[b];
+        if (m < 0 || m > context_lens[b])
+            return ORC_BAD_ARG;
+    }
+    const int T = query_start[N];
+    int status = ORC_OK;
+#ifdef _OPENMP
+    if (threads <= 0)
+        threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(threads)
+#endif
+    for (int64_t i = 0; i < (int64_t)T * H; ++i) {
+        const int row = (int)(i / H), h = (int)(i % H);
+        int b = 0;
+        while (query_start[b + 1] <= row)
+            ++b;
+        const int n = context_lens[b];
+        const int m = query_start[b + 1] - query_start[b];
+        const int32_t visible = n - m + (row - query_start[b]) + 1;   /* tokens 0..p */
+        const int rc = decode_one(out + ((int64_t)row * H + h) * D, NULL,
+                                  (const char *)q + (int64_t)row * H * D * elem_bytes(dtype),
+                                  k_pool, v_pool, block_tables + (int64_t)b * MB, &visible,
+                                  0, h, H, D, B, NB, MB, (double)scale, dtype);
         if (rc != ORC_OK) {
 #ifdef _OPENMP
 #pragma omp critical

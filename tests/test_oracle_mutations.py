@@ -2,8 +2,9 @@
 source (a dropped token, a reversed offset, a transposed layout, a missing
 scale, a wrong sign, a wrong operand, a missing normalisation, a shifted
 index, a wrong exponent bias, swapped block/offset, half a copy, mirrored
-heads, and in the swap: only K, a missed offset, mirrored heads, only the
-first pair) each make at least one pin of tests/test_oracle_pins.py fail.  The
+heads; in the swap: only K, a missed offset, mirrored heads, only the first
+pair; in the prefill: the query's own token left out, the cached prefix
+ignored, the query row taken within its chunk) each make at least one pin of tests/test_oracle_pins.py fail.  The
 mutants are built in a temporary directory on the CPU; oracle/oracle.c is
 never changed.  No GPU."""
 import os
@@ -39,6 +40,12 @@ MUTATIONS = {
                     ";"),
     "mirrored-heads-in-write": ("const int64_t src = ((int64_t)i * H + h) * D;",
                                 "const int64_t src = ((int64_t)i * H + (H - 1 - h)) * D;"),
+    "prefill-excludes-own-token": ("const int32_t visible = n - m + (row - query_start[b]) + 1;",
+                                   "const int32_t visible = n - m + (row - query_start[b]);"),
+    "prefill-ignores-prefix": ("const int32_t visible = n - m + (row - query_start[b]) + 1;",
+                               "const int32_t visible = (row - query_start[b]) + 1;"),
+    "prefill-query-row-in-chunk": ("(const char *)q + (int64_t)row * H * D * elem_bytes(dtype),",
+                                   "(const char *)q + (int64_t)(row - query_start[b]) * H * D * elem_bytes(dtype),"),
     "swap-k-only": ("memcpy((char *)dst_v + to * es, (const char *)src_v + from * es, es);", ";"),
     "swap-misses-last-offset": ("            for (int o = 0; o < B; ++o)\n                for (int d = 0; d < D; ++d) {\n                    const int64_t from",
                                 "            for (int o = 0; o < B - 1; ++o)\n                for (int d = 0; d < D; ++d) {\n                    const int64_t from"),
@@ -64,6 +71,8 @@ PINS = {
     "step-cfg1": lambda o: pins.test_step_reproduces_placement(o, lambda: W.config1()),
     "write-read-back": lambda o: pins.test_write_then_read_back(o),
     "sharing-diagram": lambda o: pins.test_sharing_diagram(o),
+    "prefill-sdpa": lambda o: [pins.test_prefill_equals_causal_sdpa(o, c) for c in range(3)],
+    "prefill-one-token": lambda o: pins.test_prefill_of_one_token_is_decode(o),
     "swap-round-trip": lambda o: pins.test_swap_round_trip_leaves_decode_unchanged(o),
     "swap-block-slices": lambda o: pins.test_swap_equals_whole_block_slices(o),
     "swap-is-copy-in-one-pool": lambda o: pins.test_swap_within_one_pool_is_copy_blocks(o),

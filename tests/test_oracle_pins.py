@@ -608,3 +608,67 @@ def test_swap_rejects(oracle_lib):
         oracle_lib.swap_blocks(dst, dst.copy(), src, src, [[6, 0]])
     with pytest.raises(oracle_lib.OracleError):          # one destination twice
         oracle_lib.swap_blocks(dst, dst.copy(), src, src, [[0, 1], [2, 1]])
+
+
+# --------------------------------------------------------------------------
+# prefill (wywy.jp Keyword "prompt phase"; WHERE, shared prefix)
+# --------------------------------------------------------------------------
+
+def causal_sdpa(k, v, q, scale):
+    """torch's causal scaled-dot-product attention in fp64 over one
+    sequence: q, k, v [n][H][D] -> [n][H][D]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64)).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                         scale=float(scale))
+    return o.permute(1, 0, 2).numpy()
+
+
+def small_prefill_cases():
+    return [W.prefill_small(),
+            W.prefill_small(seed=7, dtype=W.F32, block_size=8,
+                            groups=((0, [3]), (16, [16, 1]), (5, [30]), (0, [64]))),
+            W.prefill_mix(seed=3, num_heads=2, head_dim=64, num_seqs=4, hi=200)]
+
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_prefill_equals_causal_sdpa(oracle_lib, case):
+    """Every query row equals the matching row of torch's causal attention
+    over the whole sequence (the query at position p sees tokens 0..p);
+    for a suffix over a cached prefix, the rows are the last ones of that
+    full causal attention, whatever the prefix's own queries would be --
+    the prefix is reused, not recomputed (wywy.jp WHERE, shared prefix)."""
+    wl = small_prefill_cases()[case]
+    out = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    rng = np.random.default_rng(case)
+    for b in range(wl.num_seqs):
+        n, m = int(wl.context_lens[b]), int(wl.query_lens[b])
+        qs = int(wl.query_start[b])
+        q_full = rng.standard_normal((n, wl.num_heads, wl.head_dim))   # prefix queries: any
+        q_full[n - m:] = wl.q[qs:qs + m]
+        ref = causal_sdpa(wl.logical_k[b], wl.logical_v[b], q_full, wl.scale)[n - m:]
+        np.testing.assert_allclose(out[qs:qs + m], ref, rtol=1e-10, atol=1e-12,
+                                   err_msg=f"sequence {b}")
+
+
+def test_prefill_of_one_token_is_decode(oracle_lib):
+    """With one query per sequence (its last token) prefill is decode."""
+    wl = W.prefill_small(groups=((0, [1]), (9, [1]), (32, [1]), (47, [1])))
+    out = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    ref = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                            wl.scale)
+    assert np.array_equal(out, ref)
+
+
+def test_prefill_rejects(oracle_lib):
+    wl = W.prefill_small()
+    bad = wl.query_start.copy()
+    bad[2] = bad[1] + int(wl.context_lens[1]) + 1      # more queries than context
+    bad[3:] += bad[2] - wl.query_start[2]
+    q = np.zeros((int(bad[-1]), wl.num_heads, wl.head_dim), wl.q.dtype)
+    with pytest.raises(oracle_lib.OracleError):
+        oracle_lib.prefill(q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens, bad,
+                           wl.scale)

@@ -129,3 +129,30 @@ def test_byte_counter_closed_forms():
     # one 4-byte table entry per block in use
     ctx = np.array([1, 16, 17])
     assert W.algorithmic_bytes(ctx, 40, 128, 16, 2) == 34 * 40 * 128 * 2 * 2 + 4 * (1 + 1 + 2)
+
+
+@pytest.mark.parametrize("make", [lambda: W.prefill_small(),
+                                  lambda: W.prefill_shared(num_heads=2, head_dim=64, groups=2,
+                                                           members=3, prefix=(17, 70),
+                                                           suffix=(1, 40))])
+def test_prefill_pools_hold_the_logical_tokens(make):
+    """Gathering each sequence's tokens through its table gives its logical
+    K/V; a group's full prefix blocks are shared; no other slot holds data."""
+    wl = make()
+    B = wl.block_size
+    filled = np.zeros(wl.k_pool.shape[:1] + (B,), bool)
+    for b in range(wl.num_seqs):
+        n = int(wl.context_lens[b])
+        for t in range(n):
+            blk = int(wl.block_tables[b, t // B])
+            assert np.array_equal(wl.k_pool[blk, :, t % B].view(np.uint16 if wl.dtype == W.F16 else np.uint32),
+                                  wl.logical_k[b][t].view(np.uint16 if wl.dtype == W.F16 else np.uint32))
+            assert np.array_equal(wl.v_pool[blk, :, t % B], wl.logical_v[b][t])
+            filled[blk, t % B] = True
+    assert np.isnan(wl.k_pool[~filled]).all() and np.isnan(wl.v_pool[~filled]).all()
+    b = 0
+    for P, sufs in wl.extra["groups"]:
+        rows = wl.block_tables[b:b + len(sufs), :P // B]
+        assert (rows == rows[0]).all()
+        b += len(sufs)
+    assert int(wl.query_start[-1]) == len(wl.q)

@@ -634,3 +634,159 @@ def pressure(seed=13, dtype=F16, num_heads=4, head_dim=64, block_size=16,
                     block_size=B, num_blocks=num_blocks, num_host_blocks=num_blocks,
                     max_blocks=_blocks_for(max_len, B), scale=np.float32(1.0 / math.sqrt(D)),
                     groups=groups, gen_lens=gen_lens, prompt_keys=pk, prompt_values=pv)
+
+
+# ---------------------------------------------------------------------------
+# Prefill (prompt phase): every sequence's last tokens are queries over its
+# whole context, causally.  A group's members share a cached prefix (its
+# full blocks shared in their tables; the partial prefix block copied per
+# member, as copy-on-write leaves it) and each has its own suffix; a full
+# prefill is a group of one with an empty prefix.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    seed: int
+    dtype: str
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    context_lens: np.ndarray       # int32 [N]
+    query_start: np.ndarray        # int32 [N+1]: rows of q / out per sequence
+    block_tables: np.ndarray       # int32 [N][MB], -1 past the live entries
+    scale: np.float32
+    q: np.ndarray                  # [T][H][D]
+    k_pool: np.ndarray             # [NB][H][B][D]; NaN in every slot that holds no token
+    v_pool: np.ndarray
+    logical_k: list                # per sequence, [n][H][D]
+    logical_v: list
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self):
+        return len(self.context_lens)
+
+    @property
+    def query_lens(self):
+        return np.diff(self.query_start)
+
+    @property
+    def max_context_len(self):
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_query_len(self):
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+    @property
+    def elem_bytes(self):
+        return ELEM_BYTES[self.dtype]
+
+    def visible_tokens(self) -> int:
+        """Sum over query tokens of the keys each one attends to (p + 1)."""
+        tot = 0
+        for n, m in zip(self.context_lens.tolist(), self.query_lens.tolist()):
+            tot += m * (n - m) + m * (m + 1) // 2
+        return tot
+
+    def algorithmic_flops(self) -> int:
+        """2 D flops for q.k and 2 D for p.v per (query, visible key, head)."""
+        return 4 * self.head_dim * self.num_heads * self.visible_tokens()
+
+    def algorithmic_bytes(self) -> int:
+        """q and out once, each sequence's K and V once."""
+        H, D, s = self.num_heads, self.head_dim, self.elem_bytes
+        T = int(self.query_start[-1])
+        return 2 * T * H * D * s + 2 * int(self.context_lens.sum()) * H * D * s
+
+
+def _prefill_build(name, seed, dtype, H, D, B, groups, host=True):
+    """groups: list of (prefix_len, [suffix_len, ...])."""
+    npd = NP_DTYPES[dtype]
+    ss = np.random.SeedSequence(seed)
+    c_place, c_vals = ss.spawn(2)
+    g_streams = c_vals.spawn(len(groups))
+    ctx, qlen, plan = [], [], []
+    used = 0
+    for (P, sufs) in groups:
+        used += P // B
+        for S in sufs:
+            ctx.append(P + S)
+            qlen.append(S)
+            used += _blocks_for(P + S, B) - P // B
+    N = len(ctx)
+    NB = max(int(math.ceil(1.5 * used)), 1)
+    MB = max(max(_blocks_for(n, B) for n in ctx), 1)
+    perm = np.random.default_rng(c_place).permutation(NB)
+    tables = _empty_tables(N, MB)
+    kp = np.full((NB, H, B, D), np.nan, npd)
+    vp = np.full((NB, H, B, D), np.nan, npd)
+    logical_k, logical_v, qs = [], [], []
+    cursor, b = 0, 0
+    for gi, (P, sufs) in enumerate(groups):
+        streams = g_streams[gi].spawn(1 + len(sufs))
+        r = np.random.default_rng(streams[0])
+        pk, pv = _normal(r, (P, H, D), npd), _normal(r, (P, H, D), npd)
+        shared = perm[cursor:cursor + P // B]
+        cursor += P // B
+        for j, blk in enumerate(shared):
+            kp[blk] = pk[j * B:(j + 1) * B].transpose(1, 0, 2)
+            vp[blk] = pv[j * B:(j + 1) * B].transpose(1, 0, 2)
+        for si, S in enumerate(sufs):
+            r = np.random.default_rng(streams[1 + si])
+            sk, sv = _normal(r, (S, H, D), npd), _normal(r, (S, H, D), npd)
+            qs.append(_normal(r, (S, H, D), npd))
+            k = np.concatenate([pk, sk])
+            v = np.concatenate([pv, sv])
+            n = P + S
+            own = perm[cursor:cursor + _blocks_for(n, B) - P // B]
+            cursor += len(own)
+            row = list(shared) + list(own)
+            tables[b, :len(row)] = row
+            for j in range(P // B, len(row)):
+                lo, hi = j * B, min((j + 1) * B, n)
+                kp[row[j], :, :hi - lo] = k[lo:hi].transpose(1, 0, 2)
+                vp[row[j], :, :hi - lo] = v[lo:hi].transpose(1, 0, 2)
+            logical_k.append(k)
+            logical_v.append(v)
+            b += 1
+    q = np.concatenate(qs) if qs else np.zeros((0, H, D), npd)
+    query_start = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    return PrefillWorkload(name=name, seed=seed, dtype=dtype, num_heads=H, head_dim=D,
+                           block_size=B, num_blocks=NB,
+                           context_lens=np.asarray(ctx, dtype=np.int32), query_start=query_start,
+                           block_tables=tables, scale=np.float32(1.0 / math.sqrt(D)), q=q,
+                           k_pool=kp, v_pool=vp, logical_k=logical_k, logical_v=logical_v,
+                           extra={"groups": [(P, list(s)) for P, s in groups]})
+
+
+def prefill_mix(seed=41, dtype=F16, num_heads=40, head_dim=128, block_size=16, num_seqs=16,
+                median=300.0, sigma=0.9, lo=1, hi=2048):
+    """Full prefills of num_seqs prompts, lengths lognormal (median 300,
+    sigma 0.9, clipped to [1, 2048]: the long, varied request mix)."""
+    rng = np.random.default_rng(seed)
+    lens = lognormal_lengths(rng, num_seqs, median, sigma, lo, hi)
+    return _prefill_build("prefill-mix", seed, dtype, num_heads, head_dim, block_size,
+                          [(0, [int(n)]) for n in lens])
+
+
+def prefill_shared(seed=42, dtype=F16, num_heads=40, head_dim=128, block_size=16, groups=4,
+                   members=8, prefix=(256, 1024), suffix=(16, 256)):
+    """Shared prefixes (a long system prompt or few-shot examples) cached
+    once per group; each member's own suffix tokens are the queries."""
+    rng = np.random.default_rng(seed)
+    spec = []
+    for _ in range(groups):
+        P = int(rng.integers(prefix[0], prefix[1] + 1))
+        spec.append((P, [int(x) for x in rng.integers(suffix[0], suffix[1] + 1, size=members)]))
+    return _prefill_build("prefill-shared", seed, dtype, num_heads, head_dim, block_size, spec)
+
+
+def prefill_small(seed=43, dtype=F16, num_heads=2, head_dim=64, block_size=16,
+                  groups=((0, [1]), (0, [17]), (0, [40]), (21, [1, 5]), (48, [33]))):
+    """A few short cases: one token, ragged tails, a prefix ending mid-block
+    shared by two members, a prefix on a block boundary."""
+    return _prefill_build("prefill-small", seed, dtype, num_heads, head_dim, block_size,
+                          [(P, list(s)) for P, s in groups])
