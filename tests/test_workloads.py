@@ -149,7 +149,9 @@ def test_prefill_pools_hold_the_logical_tokens(make):
                                   wl.logical_k[b][t].view(np.uint16 if wl.dtype == W.F16 else np.uint32))
             assert np.array_equal(wl.v_pool[blk, :, t % B], wl.logical_v[b][t])
             filled[blk, t % B] = True
-    assert np.isnan(wl.k_pool[~filled]).all() and np.isnan(wl.v_pool[~filled]).all()
+    by_slot = lambda pool: pool.transpose(0, 2, 1, 3)          # [NB][B][H][D]
+    assert np.isnan(by_slot(wl.k_pool)[~filled]).all()
+    assert np.isnan(by_slot(wl.v_pool)[~filled]).all()
     b = 0
     for P, sufs in wl.extra["groups"]:
         rows = wl.block_tables[b:b + len(sufs), :P // B]
