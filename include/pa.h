@@ -193,6 +193,45 @@ int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
                    int num_blocks, int dtype, void *stream);
 
 /*
+ * Paged prefill attention (the prompt phase).  Source: the PagedAttention
+ * pages -- the wywy.jp notes, Keyword "prompt phase" (all prompt tokens are
+ * known, so they are processed together, matrix-matrix) and WHERE, shared
+ * prefix (a cached prefix's KV is reused; only the request's own tokens are
+ * computed); the zhaifeiyue.github.io summary, method paragraph, block-wise
+ * attention equation, with each query's context cut at its own position.
+ *
+ *   sequence b holds n_b = context_lens[b] tokens in the pools (their K/V
+ *   already written, e.g. by pa_write_kv); its last m_b = query_start[b+1]
+ *   - query_start[b] tokens are queries, rows query_start[b] ..
+ *   query_start[b+1]-1 of q and out.  Query i sits at position
+ *   p = n_b - m_b + i and
+ *     out[row][h][:] = sum_{t<=p} softmax_t(scale * q[row][h] . K_t[h]) V_t[h]
+ *   with K_t / V_t read through block_tables as in pa_decode.
+ *
+ * q, out: [num_query_rows][num_heads][head_dim] fp16, 16-byte aligned.
+ * query_start: int32 [num_seqs + 1], non-decreasing from 0.  Pools, tables
+ * and context_lens as in pa_decode.  max_context_len (>= every context
+ * length; context lengths above it are clamped to it; at most
+ * max_blocks_per_seq * block_size) and max_query_len (>= every m_b, at most
+ * max_context_len) are host-side bounds that size the grid.
+ * Only PA_F16 (PA_ERR_UNSUPPORTED otherwise); head_dim 64 or 128; block_size
+ * 8, 16, 32 or 64.  The products run on MFMA with fp32 accumulation and an
+ * fp32 softmax; the attention weights are rounded to fp16 for the product
+ * with V.
+ *
+ * A sequence whose m_b exceeds its (clamped) context, or whose rows fall
+ * outside [0, num_query_rows), gets NaN rows (those in range); a table entry
+ * outside the pool makes NaN every row that attends to its keys.  Rows past
+ * max_query_len of a sequence are not written.  No workspace.  Asynchronous
+ * on `stream`.
+ */
+int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, int num_seqs, int num_query_rows, int num_heads,
+               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+               int max_context_len, int max_query_len, float scale, int dtype, void *stream);
+
+/*
  * Swapping: copy whole blocks between two pool pairs, typically the device
  * pools and pinned host pools (swap out: device -> host; swap in: host ->
  * device).  Source: the PagedAttention pages -- the wywy.jp notes, Keyword

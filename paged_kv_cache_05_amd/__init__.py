@@ -41,7 +41,7 @@ def default_partition(max_context_len: int) -> int:
 
 # Every symbol include/pa.h and include/pa_manager.h declare.
 EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
-           "pa_copy_blocks", "pa_swap_blocks", "pa_status_string", "pa_last_error",
+           "pa_copy_blocks", "pa_swap_blocks", "pa_prefill", "pa_status_string", "pa_last_error",
            "pa_manager_create", "pa_manager_destroy", "pa_manager_add", "pa_manager_fork",
            "pa_manager_append", "pa_manager_free", "pa_manager_tables", "pa_manager_num_free",
            "pa_manager_num_sequences", "pa_manager_refcount", "pa_manager_length",
@@ -95,6 +95,9 @@ def library() -> ctypes.CDLL:
     lib.pa_write_kv.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                               i32, i32, f32, i32, vp]
+    lib.pa_prefill.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -284,3 +287,32 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
         _reachable(src_v, "src_v"), _reachable(block_mapping, "block_mapping", torch.int64),
         block_mapping.shape[0], H, D, B, sNB, dNB, _dtype_code(src_k), _stream(stream))
     _check(rc, "pa_swap_blocks")
+
+
+def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+               max_context_len, max_query_len, stream=None):
+    """out[T][H][D] = causal paged prefill attention of q[T][H][D]: sequence
+    b's rows query_start[b] .. query_start[b+1]-1 are the last tokens of its
+    context_lens[b]-token context (int32 device tensors; query_start [N+1]).
+    max_context_len and max_query_len are host-side bounds."""
+    import torch
+    NB, H, B, D = k_pool.shape
+    T = q.shape[0]
+    N = context_lens.shape[0]
+    if tuple(q.shape) != (T, H, D) or tuple(out.shape) != (T, H, D):
+        raise PAError("pa_prefill: q / out must be [T][H][D] matching the pools")
+    if tuple(query_start.shape) != (N + 1,):
+        raise PAError("pa_prefill: query_start must be [num_seqs + 1]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != N:
+        raise PAError("pa_prefill: block_tables must be [num_seqs][max_blocks]")
+    for t, name in ((q, "q"), (out, "out"), (v_pool, "v_pool")):
+        if t.dtype != k_pool.dtype:
+            raise PAError(f"pa_prefill: {name} must be {k_pool.dtype}")
+    rc = library().pa_prefill(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), N, T, H, D, B, NB,
+        block_tables.shape[1], int(max_context_len), int(max_query_len), float(scale),
+        _dtype_code(q), _stream(stream))
+    _check(rc, "pa_prefill")

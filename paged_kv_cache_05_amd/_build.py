@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_cache.hip", "pa_manager.cpp"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_manager.cpp"]
 LIBRARY = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 

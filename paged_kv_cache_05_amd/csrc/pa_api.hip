@@ -176,6 +176,48 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 
 extern "C" {
 
+int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, int num_seqs, int num_query_rows, int num_heads,
+               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+               int max_context_len, int max_query_len, float scale, int dtype, void *stream) {
+  int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
+  if (rc != PA_OK) return rc;
+  if (dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_query_rows < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+      max_query_len < 0 || max_query_len > max_context_len ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size || !(scale == scale))
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_query_rows == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)query_start & 3u))
+    return PA_ERR_SHAPE;
+  const int64_t tiles = ((int64_t)max_query_len + pa::prefill_query_tile() - 1) /
+                        pa::prefill_query_tile();
+  if (num_heads > 0x7fffffff || tiles > 65535 || num_seqs > 65535) return PA_ERR_SHAPE;
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.num_heads = num_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.num_query_rows = num_query_rows;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  return launch_checked("pa_prefill", [&] {
+    return pa::launch_prefill(p, num_seqs, head_dim, block_size, max_query_len,
+                              static_cast<hipStream_t>(stream));
+  });
+}
+
 int pa_swap_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
                    const int64_t *block_mapping, int num_pairs, int num_heads, int head_dim,
                    int block_size, int src_num_blocks, int dst_num_blocks, int dtype,

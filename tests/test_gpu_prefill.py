@@ -1,0 +1,149 @@
+"""GPU parity of pa_prefill (paged causal prefill on MFMA) against the
+oracle's prefill, on the same seeded inputs, through the C ABI.
+
+Bar: elementwise |gpu - oracle| <= 2e-3 + 1e-2 |oracle| (fp16 K/V/q; the
+attention weights are rounded to fp16 for the product with V, an error of
+at most 2^-11 relative per weight, far inside the bar).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ABS, REL = 2e-3, 1e-2
+
+
+def announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def run_gpu(pa, wl, device, q=None, query_start=None, context_lens=None, tables=None,
+            max_query_len=None, k_pool=None):
+    q = wl.q if q is None else q
+    qs = wl.query_start if query_start is None else query_start
+    ctx = wl.context_lens if context_lens is None else context_lens
+    tables = wl.block_tables if tables is None else tables
+    dq = dev(q, device)
+    out = torch.full_like(dq, float("nan"))
+    mq = int(np.diff(qs).max()) if len(qs) > 1 else 0
+    pa.pa_prefill(out, dq, dev(wl.k_pool if k_pool is None else k_pool, device),
+                  dev(wl.v_pool, device), dev(tables, device), dev(ctx, device), dev(qs, device),
+                  float(wl.scale), max(int(np.max(ctx)) if len(ctx) else 0, 1),
+                  mq if max_query_len is None else max_query_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(gpu, ref, where):
+    gpu = gpu.astype(np.float64)
+    bad = ~(np.abs(gpu - ref) <= ABS + REL * np.abs(ref))
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{where}: {bad.sum()} of {bad.size} out of tolerance; first {i}: "
+                             f"gpu {gpu[i]!r} oracle {ref[i]!r}")
+
+
+CASES = {
+    "small-b16-d64": lambda: W.prefill_small(),
+    "small-b8-d128": lambda: W.prefill_small(seed=5, head_dim=128, block_size=8),
+    "small-b32-d64": lambda: W.prefill_small(seed=6, block_size=32,
+                                             groups=((0, [130]), (33, [2, 97]), (64, [64]))),
+    "small-b64-d128": lambda: W.prefill_small(seed=7, head_dim=128, block_size=64,
+                                              groups=((0, [129]), (100, [1, 28]), (0, [2]))),
+    "mix": lambda: W.prefill_mix(seed=8, num_heads=4, num_seqs=6, hi=700),
+    "shared": lambda: W.prefill_shared(seed=9, num_heads=3, groups=2, members=4,
+                                       prefix=(100, 400), suffix=(1, 200)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_matches_oracle(pa, oracle_lib, device, name):
+    announce(f"prefill parity {name}")
+    wl = CASES[name]()
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(run_gpu(pa, wl, device), ref, name)
+
+
+def test_prefill_edges(pa, oracle_lib, device):
+    """Sequences with no queries beside one-token and tile-boundary chunks
+    (127, 128, 129 queries); rows of empty chunks are never written."""
+    announce("prefill edges")
+    wl = W.prefill_small(seed=11, head_dim=128,
+                         groups=((0, [127]), (5, [0]), (0, [128]), (200, [0, 129]), (0, [1])))
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(run_gpu(pa, wl, device), ref, "edges")
+
+
+def test_prefill_poisons_rows_that_see_a_bad_block(pa, oracle_lib, device):
+    """A table entry outside the pool: rows whose context reaches that
+    block are NaN, every other row is still right."""
+    announce("prefill bad table entry")
+    wl = W.prefill_small(seed=12, groups=((0, [70]), (0, [40])))
+    B = wl.block_size
+    tables = wl.block_tables.copy()
+    tables[0, 2] = wl.num_blocks + 3            # keys 32..47 of sequence 0
+    got = run_gpu(pa, wl, device, tables=tables)
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    n0 = int(wl.context_lens[0])
+    pos = np.arange(n0)                          # sequence 0 is a full prefill
+    sees = pos >= 2 * B
+    assert np.isnan(got[:n0][sees]).all()
+    check(got[:n0][~sees], ref[:n0][~sees], "rows before the bad block")
+    check(got[n0:], ref[n0:], "other sequence")
+
+
+def test_prefill_chunk_longer_than_context_is_nan(pa, oracle_lib, device):
+    announce("prefill bad chunk")
+    wl = W.prefill_small(seed=13, groups=((10, [5]), (0, [9])))
+    ctx = wl.context_lens.copy()
+    ctx[0] = 3                                   # 5 queries, 3 tokens: invalid
+    got = run_gpu(pa, wl, device, context_lens=ctx)
+    assert np.isnan(got[:5]).all()
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(got[5:], ref[5:], "valid sequence")
+
+
+def sampled_rows(wl, per_seq, rng):
+    """(sequence, first row, count) windows whose oracle values need only a
+    truncated context: a query at position p sees tokens 0..p."""
+    out = []
+    for b in range(wl.num_seqs):
+        m = int(wl.query_lens[b])
+        if m == 0:
+            continue
+        starts = {0, max(m - per_seq, 0)} | {int(x) for x in rng.integers(0, m, size=2)}
+        for s in sorted(starts):
+            out.append((b, s, min(per_seq, m - s)))
+    return out
+
+
+@pytest.mark.parametrize("which", ["mix", "shared"])
+def test_prefill_full_size_sampled(pa, oracle_lib, device, which):
+    """The OPT-13B-shaped workloads (40 heads x 128, B 16) in one launch;
+    windows of rows checked against the oracle on truncated contexts."""
+    announce(f"prefill full size {which}")
+    wl = W.prefill_mix() if which == "mix" else W.prefill_shared()
+    got = run_gpu(pa, wl, device)
+    rng = np.random.default_rng(17)
+    for b, s, k in sampled_rows(wl, 6, rng):
+        n, m = int(wl.context_lens[b]), int(wl.query_lens[b])
+        qs = int(wl.query_start[b])
+        n_cut = n - m + s + k                    # context through the window's last query
+        ref = oracle_lib.prefill(wl.q[qs + s:qs + s + k], wl.k_pool, wl.v_pool,
+                                 wl.block_tables[b:b + 1], np.array([n_cut], np.int32),
+                                 np.array([0, k], np.int32), wl.scale)
+        check(got[qs + s:qs + s + k], ref, f"sequence {b} rows {s}..{s + k - 1}")
