@@ -23,6 +23,8 @@ the host block manager drives (parallel sampling with beam-like pruning at
 the same layer shape, every step over all L layers) and prints its own line.
 ``--workload swap`` times block swapping between the device pool and a
 pinned host pool against the block size and prints its own line.
+``--workload prefill`` times paged prefill attention (MFMA) on a full
+prompt mix and on shared-prefix requests and prints its own line.
 """
 import argparse
 import hashlib
@@ -82,6 +84,104 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "torch.mul fp32 copy", "read_bytes": 4 * n,
                       "write_bytes": 4 * n}), flush=True)
+    return 0
+
+
+PEAK_FP16_TFLOPS = 2500.0   # dense fp16 MFMA, MI355X
+
+
+def bench_prefill(args):
+    """Paged prefill at the OPT-13B layer shape (40 heads x head_dim 128,
+    fp16, B = 16): (a) full prefill of 16 prompts, lengths lognormal
+    (median 300, sigma 0.9, clipped [1, 2048]); (b) 4 groups x 8 requests
+    sharing a cached prefix of 256..1024 tokens, each with its own 16..256
+    query tokens.  Throughput = causal attention FLOPs (4 D per query, key
+    and head) / event-timed call."""
+    import torch
+
+    import paged_kv_cache_05_amd as pa
+    import workloads as W
+
+    device = torch.device("cuda:0")
+    K = max(1, min(args.steps, 50))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, wl in (("mix", W.prefill_mix()), ("shared", W.prefill_shared())):
+        q, kp, vp = dev(wl.q), dev(wl.k_pool), dev(wl.v_pool)
+        tables, ctx, qs = dev(wl.block_tables), dev(wl.context_lens), dev(wl.query_start)
+        out = torch.empty_like(q)
+        call = lambda: pa.pa_prefill(out, q, kp, vp, tables, ctx, qs, float(wl.scale),
+                                     wl.max_context_len, wl.max_query_len,
+                                     host_query_start=wl.query_start,
+                                     host_context_lens=wl.context_lens)
+        for _ in range(max(args.warmup, 1)):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        flops, nbytes = wl.algorithmic_flops(), wl.algorithmic_bytes()
+        got = out.cpu().numpy()
+        if not np.isfinite(got).all():
+            raise SystemExit(f"bench: non-finite prefill output ({name})")
+        res[name] = {"wl": wl, "ms": float(ms.mean()), "flops": flops, "bytes": nbytes,
+                     "out": got}
+    mix = res["mix"]
+    tflops = mix["flops"] / (mix["ms"] * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        if not os.path.exists(oracle.LIBRARY):
+            oracle.build()
+        wl = mix["wl"]
+        threads = oracle.threads_available()
+        # sample: the last 64 query rows of the longest prompt (the most keys each)
+        b = int(np.argmax(wl.context_lens))
+        n, m, q0 = int(wl.context_lens[b]), int(wl.query_lens[b]), int(wl.query_start[b])
+        k = min(64, m)
+        t = time.perf_counter()
+        ref = oracle.prefill(wl.q[q0 + m - k:q0 + m], wl.k_pool, wl.v_pool,
+                             wl.block_tables[b:b + 1], np.array([n], np.int32),
+                             np.array([0, k], np.int32), wl.scale, threads=threads)
+        secs = time.perf_counter() - t
+        sample_flops = 4 * wl.head_dim * wl.num_heads * sum(n - k + i + 1 for i in range(k))
+        cpu = {"value": round(sample_flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"last {k} query rows of the {n}-token prompt, fp64, {secs:.2f} s"}
+        got = mix["out"][q0 + m - k:q0 + m].astype(np.float64)
+        cpu["parity"] = bool(np.all(np.abs(got - ref) <= 2e-3 + 1e-2 * np.abs(ref)))
+
+    sh = res["shared"]
+    rec = {
+        "metric": "paged prefill attention TFLOP/s (causal, MFMA fp16), OPT-13B layer shape",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(mix["ms"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded; lognormal prompt lengths, N(0,1) q/K/V, scattered blocks)",
+        "config": {"workload": "full prefill of 16 prompts, lognormal lengths median 300 "
+                               "clipped [1,2048], 40 heads x 128, block 16",
+                   "sum_prompt": int(mix["wl"].context_lens.sum()),
+                   "max_prompt": mix["wl"].max_context_len,
+                   "algorithmic_gflop": round(mix["flops"] / 1e9, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_listed_kernel<128,16>"},
+        "hbm_GBps_algorithmic": round(mix["bytes"] / (mix["ms"] * 1e-3) / 1e9, 1),
+        "shared_prefix": {"ms": round(sh["ms"], 5),
+                          "TFLOPs": round(sh["flops"] / (sh["ms"] * 1e-3) / 1e12, 2),
+                          "query_tokens": int(sh["wl"].query_start[-1]),
+                          "context_tokens": int(sh["wl"].context_lens.sum()),
+                          "groups": sh["wl"].extra["groups"].__len__()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
     return 0
 
 
@@ -315,10 +415,12 @@ def main():
                     help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
-    ap.add_argument("--workload", choices=["decode", "generation", "swap"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "generation", "swap", "prefill"],
+                    default="decode",
                     help="decode: one layer's decode step (the default line); generation: the "
                          "block-manager decoding loop over all layers; swap: block swap "
-                         "device <-> pinned host against the block size")
+                         "device <-> pinned host against the block size; prefill: paged "
+                         "prefill attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus "
@@ -331,6 +433,8 @@ def main():
         return bench_generation(args)
     if args.workload == "swap":
         return bench_swap(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
 
     import torch
 

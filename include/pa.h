@@ -219,6 +219,15 @@ int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
  * fp32 softmax; the attention weights are rounded to fp16 for the product
  * with V.
  *
+ * host_query_start (optional, host memory, num_seqs + 1 entries) is a host
+ * copy of query_start: with it the library launches only the query tiles
+ * that exist, heaviest first (the tiles whose queries see the most keys),
+ * when there are at most 960 of them; host_context_lens (optional, host
+ * memory) then refines that order.  Without them, or with more tiles, the
+ * grid covers every (head, tile < max_query_len / 128, sequence) and empty
+ * tiles exit at once.  A sequence's device query count must not exceed its
+ * host one.  Results do not depend on the launch form.
+ *
  * A sequence whose m_b exceeds its (clamped) context, or whose rows fall
  * outside [0, num_query_rows), gets NaN rows (those in range); a table entry
  * outside the pool makes NaN every row that attends to its keys.  Rows past
@@ -229,7 +238,9 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                const int32_t *block_tables, const int32_t *context_lens,
                const int32_t *query_start, int num_seqs, int num_query_rows, int num_heads,
                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-               int max_context_len, int max_query_len, float scale, int dtype, void *stream);
+               int max_context_len, int max_query_len, float scale, int dtype,
+               const int32_t *host_query_start, const int32_t *host_context_lens,
+               void *stream);
 
 /*
  * Swapping: copy whole blocks between two pool pairs, typically the device

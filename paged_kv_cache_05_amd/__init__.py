@@ -96,7 +96,7 @@ def library() -> ctypes.CDLL:
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                               i32, i32, f32, i32, vp]
+                               i32, i32, f32, i32, vp, vp, vp]
     lib.pa_prefill.restype = i32
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_swap_blocks.restype = i32
@@ -290,11 +290,15 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
 
 
 def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
-               max_context_len, max_query_len, stream=None):
+               max_context_len, max_query_len, stream=None, host_query_start=None,
+               host_context_lens=None):
     """out[T][H][D] = causal paged prefill attention of q[T][H][D]: sequence
     b's rows query_start[b] .. query_start[b+1]-1 are the last tokens of its
     context_lens[b]-token context (int32 device tensors; query_start [N+1]).
-    max_context_len and max_query_len are host-side bounds."""
+    max_context_len and max_query_len are host-side bounds; host copies of
+    query_start (and context_lens) let the library launch only the tiles
+    that exist, heaviest first."""
+    import numpy as np
     import torch
     NB, H, B, D = k_pool.shape
     T = q.shape[0]
@@ -308,11 +312,26 @@ def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, 
     for t, name in ((q, "q"), (out, "out"), (v_pool, "v_pool")):
         if t.dtype != k_pool.dtype:
             raise PAError(f"pa_prefill: {name} must be {k_pool.dtype}")
+    hqs = _host_i32(host_query_start, N + 1, "host_query_start")
+    hctx = _host_i32(host_context_lens, N, "host_context_lens")
     rc = library().pa_prefill(
         _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
         _dev(block_tables, "block_tables", torch.int32),
         _dev(context_lens, "context_lens", torch.int32),
         _dev(query_start, "query_start", torch.int32), N, T, H, D, B, NB,
         block_tables.shape[1], int(max_context_len), int(max_query_len), float(scale),
-        _dtype_code(q), _stream(stream))
+        _dtype_code(q), None if hqs is None else hqs.ctypes.data,
+        None if hctx is None else hctx.ctypes.data, _stream(stream))
     _check(rc, "pa_prefill")
+
+
+
+def _host_i32(a, n, name):
+    """A contiguous int32 host copy (kept alive by the caller for the call)."""
+    import numpy as np
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    if arr.shape != (n,):
+        raise PAError(f"{name} must have {n} entries")
+    return arr

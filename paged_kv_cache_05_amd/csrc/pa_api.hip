@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "pa.h"
 #include "pa_manager.h"
@@ -176,17 +177,49 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 
 extern "C" {
 
+// Work list of the prefill: every (sequence, query tile) that the grid
+// would cover, heaviest first (keys the tile's last query sees, descending;
+// ties in natural order).  False if it does not fit a WorkList.
+bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max_context_len,
+                  int max_query_len, pa::WorkList *items) {
+  const int tile = pa::prefill_query_tile();
+  const int max_tiles = (max_query_len + tile - 1) / tile;
+  struct Item {
+    uint32_t code;
+    int64_t work;
+  };
+  std::vector<Item> list;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int m = hqs[b + 1] - hqs[b];
+    if (m <= 0) continue;
+    const int n = hctx ? std::min(std::max(hctx[b], 0), max_context_len) : m;
+    const int tiles = std::min((m + tile - 1) / tile, max_tiles);
+    for (int t = 0; t < tiles; ++t) {
+      if (list.size() >= (size_t)pa::kMaxListed || b > 0xffff) return false;
+      list.push_back({(uint32_t)b << 16 | (uint32_t)t,
+                      (int64_t)n - m + std::min(m, (t + 1) * tile)});
+    }
+  }
+  std::stable_sort(list.begin(), list.end(),
+                   [](const Item &a, const Item &b) { return a.work > b.work; });
+  items->count = (int)list.size();
+  for (size_t i = 0; i < list.size(); ++i) items->item[i] = list[i].code;
+  return true;
+}
+
 int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                const int32_t *block_tables, const int32_t *context_lens,
                const int32_t *query_start, int num_seqs, int num_query_rows, int num_heads,
                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
-               int max_context_len, int max_query_len, float scale, int dtype, void *stream) {
+               int max_context_len, int max_query_len, float scale, int dtype,
+               const int32_t *host_query_start, const int32_t *host_context_lens,
+               void *stream) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
   if (dtype != PA_F16) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_query_rows < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       max_query_len < 0 || max_query_len > max_context_len ||
-      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size || !(scale == scale))
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size || !isfinite(scale))
     return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_query_rows == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
@@ -197,7 +230,7 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
     return PA_ERR_SHAPE;
   const int64_t tiles = ((int64_t)max_query_len + pa::prefill_query_tile() - 1) /
                         pa::prefill_query_tile();
-  if (num_heads > 0x7fffffff || tiles > 65535 || num_seqs > 65535) return PA_ERR_SHAPE;
+  if (tiles > kGridYZ || num_seqs > kGridYZ) return PA_ERR_SHAPE;
   pa::PrefillParams p{};
   p.out = out;
   p.q = q;
@@ -212,9 +245,13 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
   p.max_context_len = max_context_len;
   p.num_query_rows = num_query_rows;
   p.scale_log2 = scale * 1.44269504088896340736f;
+  pa::WorkList items;
+  const bool listed = host_query_start &&
+                      plan_prefill(host_query_start, host_context_lens, num_seqs,
+                                   max_context_len, max_query_len, &items);
   return launch_checked("pa_prefill", [&] {
     return pa::launch_prefill(p, num_seqs, head_dim, block_size, max_query_len,
-                              static_cast<hipStream_t>(stream));
+                              listed ? &items : nullptr, static_cast<hipStream_t>(stream));
   });
 }
 

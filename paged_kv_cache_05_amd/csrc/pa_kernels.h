@@ -84,7 +84,9 @@ struct PrefillParams {
 };
 
 int prefill_query_tile();
+// items: (sequence << 16 | query tile) in launch order, or nullptr for the
+// grid over (heads, tiles, sequences).
 hipError_t launch_prefill(const PrefillParams &p, int num_seqs, int head_dim, int block_size,
-                          int max_query_len, hipStream_t stream);
+                          int max_query_len, const WorkList *items, hipStream_t stream);
 
 }  // namespace pa

@@ -12,18 +12,26 @@
 //
 // One workgroup = one (head, sequence, tile of 128 queries); 4 waves of 32
 // queries each.  Per 32-key tile, on v_mfma_f32_32x32x16_f16:
-//   * S^T = K Q^T: the key rows are the A operand, read straight from the
-//     pool (16-byte loads along head_dim), the wave's 32 query rows the B
-//     operand.  The contraction over head_dim runs in a permuted order that
-//     both operands share (lane group g takes the half [g*D/2, (g+1)*D/2)),
-//     so that each lane reads one contiguous half row.
+//   * S^T = K Q^T: key rows are the A operand, the wave's 32 query rows the
+//     B operand (kept in registers for the whole loop).  The contraction
+//     over head_dim runs in a permuted order both operands share (lane
+//     group g takes the half [g*D/2, (g+1)*D/2)), so each lane reads one
+//     contiguous half row.
 //   * In the accumulator layout every lane holds 16 scores of one query
-//     (its column), so the online softmax needs one exchange (lanes l and
-//     l ^ 32) per tile, and rescaling the output is a per-lane multiply.
+//     (its column): the online softmax needs one exchange (lanes l, l ^ 32)
+//     per tile and rescaling the output is a per-lane multiply.
 //   * O^T += V^T P^T: P^T is the B operand straight from the score
-//     registers (converted to fp16, no shuffle); the key order that layout
-//     implies is matched by the A operand, V^T, read from LDS, where the
-//     workgroup stages each V tile transposed.
+//     registers (converted to fp16, no shuffle); the key order this implies
+//     is matched by the A operand, V^T, read from LDS.
+// The workgroup's block-table entries are copied to LDS once, so the address
+// of every key row is one LDS read away.  K and V tiles go through LDS,
+// double-buffered: the next tile's global
+// loads are in flight while the current tile's products run, and one
+// barrier per tile separates the two buffers.  K is stored row-major with a
+// 68-dword row (16-byte reads by 16 lanes hit 64 distinct banks); V is
+// stored transposed, written as packed key pairs (32-bit stores) into rows
+// of 18 dwords, which keeps both the pair writes and the 8-byte operand
+// reads free of bank conflicts.
 // Accumulation and the softmax are fp32; P is rounded to fp16 for the
 // second product.
 #include <math.h>
@@ -35,26 +43,137 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
+typedef unsigned uint8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;                 // queries per wave
 constexpr int kQTile = kWaves * kRows;    // queries per workgroup
 constexpr int kKeys = 32;                 // keys per tile
-constexpr int kVtStride = kKeys + 8;      // LDS row of V^T (halves), padded
+constexpr int kTabCache = 2048;           // block-table entries kept in LDS
+
+template <int D>
+struct Lds {
+  static constexpr int kRowK = D + 8;             // halves per K row (68 dwords at D = 128)
+  static constexpr int kRowV = kKeys + 4;         // halves per V^T row (18 dwords)
+  static constexpr int kK = kKeys * kRowK;        // halves per K buffer
+  static constexpr int kV = D * kRowV;            // halves per V^T buffer
+  // one tile: K chunks (16 bytes of one key row) and V units (8 head-dim
+  // values of a key pair); per thread, rounded up (the last round guarded)
+  static constexpr int kKUnits = kKeys * (D / 8);                // 512 at D = 128
+  static constexpr int kVUnits = (kKeys / 2) * (D / 8);          // 256 at D = 128
+  static constexpr int kKChunks = (kKUnits + kThreads - 1) / kThreads;
+  static constexpr int kVPairs = (kVUnits + kThreads - 1) / kThreads;
+};
 
 __device__ inline half8 load_half8(const _Float16 *p) {
   return *reinterpret_cast<const half8 *>(p);
 }
 
 template <int D, int B>
-__global__ void __launch_bounds__(kWaves * 64)
-prefill_kernel(const PrefillParams p) {
-  __shared__ _Float16 vt[D * kVtStride];
+struct TileLoads {
+  half8 k[Lds<D>::kKChunks];
+  half8 v[Lds<D>::kVPairs][2];
+  bool kok[Lds<D>::kKChunks], kbad[Lds<D>::kKChunks];
+  bool vok[Lds<D>::kVPairs][2];
+};
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.z;
-  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;   // longest tiles first
+// Global -> registers for keys t0 .. t0+31; keys at or past `end` (the
+// workgroup's last query position + 1) are not read and stage as zeros, and
+// a key whose table entry lies outside the pool stages as NaN (K) / zero
+// (V).  Straight-line code: every table entry is read first, then every
+// row load is issued (from the pool's first row where the key is not
+// read, so that no load is conditional), so the loads overlap each other
+// and the current tile's products.  The table entry comes from the
+// workgroup's LDS copy when the whole row fits there (kLdsTable), else from
+// global memory; the two are separate instantiations, since a pointer that
+// could be either becomes a flat load whose wait also drains every global
+// load in flight.
+template <int D, int B, bool kLdsTable>
+__device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
+                                  const __attribute__((address_space(3))) int32_t *tab, int h,
+                                  int end, int t0, TileLoads<D, B> &r) {
+  const _Float16 *kh = static_cast<const _Float16 *>(p.k_pool);
+  const _Float16 *vh = static_cast<const _Float16 *>(p.v_pool);
+  constexpr int NK = Lds<D>::kKChunks, NV = Lds<D>::kVPairs;
+  int kt[NK], kd[NK], vt[NV][2], vd[NV];
+  int32_t kphys[NK], vphys[NV][2];
+#pragma unroll
+  for (int u = 0; u < NK; ++u) {
+    const int chunk = threadIdx.x + u * kThreads;   // d-chunk fastest: coalesced rows
+    kt[u] = chunk < Lds<D>::kKUnits ? t0 + chunk / (D / 8) : end;
+    kd[u] = (chunk % (D / 8)) * 8;
+    const int j = kt[u] < end ? kt[u] / B : 0;
+    kphys[u] = kLdsTable ? tab[j] : table[j];
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int unit = threadIdx.x + u * kThreads;    // key pair fastest
+    vd[u] = (unit / (kKeys / 2)) * 8;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      vt[u][s] = unit < Lds<D>::kVUnits ? t0 + 2 * (unit % (kKeys / 2)) + s : end;
+      const int j = vt[u][s] < end ? vt[u][s] / B : 0;
+      vphys[u][s] = kLdsTable ? tab[j] : table[j];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NK; ++u) {
+    const bool in = kt[u] < end;
+    const bool ok = in && kphys[u] >= 0 && kphys[u] < p.num_blocks;
+    r.kok[u] = ok;
+    r.kbad[u] = in && !ok;
+    const int64_t row = ok ? ((int64_t)kphys[u] * p.num_heads + h) * B + kt[u] % B : 0;
+    r.k[u] = load_half8(kh + row * D + kd[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bool ok = vt[u][s] < end && vphys[u][s] >= 0 && vphys[u][s] < p.num_blocks;
+      r.vok[u][s] = ok;
+      const int64_t row = ok ? ((int64_t)vphys[u][s] * p.num_heads + h) * B + vt[u][s] % B : 0;
+      r.v[u][s] = load_half8(vh + row * D + vd[u]);
+    }
+}
+
+// Registers -> LDS buffers (K row-major, V transposed as key pairs).
+template <int D, int B>
+__device__ inline void store_tile(const TileLoads<D, B> &r, _Float16 *ks, _Float16 *vs) {
+#pragma unroll
+  for (int u = 0; u < Lds<D>::kKChunks; ++u) {
+    const int chunk = threadIdx.x + u * kThreads;
+    if (chunk < Lds<D>::kKUnits) {
+      const int key = chunk / (D / 8), d0 = (chunk % (D / 8)) * 8;
+      half8 v = r.kok[u] ? r.k[u] : half8{};
+      if (r.kbad[u]) v = half8{} + (_Float16)NAN;   // NaN for every query that sees it
+      *reinterpret_cast<half8 *>(ks + key * Lds<D>::kRowK + d0) = v;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < Lds<D>::kVPairs; ++u) {
+    const int unit = threadIdx.x + u * kThreads;
+    if (unit < Lds<D>::kVUnits) {
+      const int kp = unit % (kKeys / 2), d0 = (unit / (kKeys / 2)) * 8;
+      // word e = (key 2kp, key 2kp+1) at head-dim d0 + e
+      const half8 v0 = r.vok[u][0] ? r.v[u][0] : half8{};
+      const half8 v1 = r.vok[u][1] ? r.v[u][1] : half8{};
+      const half16 z = __builtin_shufflevector(v0, v1, 0, 8, 1, 9, 2, 10, 3, 11,
+                                               4, 12, 5, 13, 6, 14, 7, 15);
+      const uint8v words = __builtin_bit_cast(uint8v, z);
+      unsigned *col = reinterpret_cast<unsigned *>(vs + d0 * Lds<D>::kRowV + 2 * kp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) col[e * (Lds<D>::kRowV / 2)] = words[e];
+    }
+  }
+}
+
+template <int D, int B, bool kLdsTable>
+__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Float16 *lds,
+                             __attribute__((address_space(3))) int32_t *tab) {
+  using L = Lds<D>;
   const int q0 = p.query_start[b];
   const int m = p.query_start[b + 1] - q0;
   const int n = min(max(p.context_lens[b], 0), p.max_context_len);
@@ -68,20 +187,15 @@ prefill_kernel(const PrefillParams p) {
   const int r = qt * kQTile + w * kRows + c;         // query index in the chunk
   const bool q_ok = r < m && !bad_seq;
   const int pos = n - m + r;                         // its position in the sequence
-  // keys the workgroup needs: up to its last query's position
   const int last = min(m, (qt + 1) * kQTile) - 1;
-  const int kv_end = bad_seq ? 0 : n - m + last + 1;
-
-  const _Float16 *qh = static_cast<const _Float16 *>(p.q);
-  const _Float16 *kh = static_cast<const _Float16 *>(p.k_pool);
-  const _Float16 *vh = static_cast<const _Float16 *>(p.v_pool);
+  const int kv_end = bad_seq ? 0 : n - m + last + 1; // keys the workgroup needs
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
-  // B operand of S^T: q row r, head-dim half g, in 16-element k-steps.
   constexpr int kSteps = D / 16;
   half8 qb[kSteps];
   {
-    const _Float16 *row = qh + ((int64_t)(q0 + r) * p.num_heads + h) * D + g * (D / 2);
+    const _Float16 *row = static_cast<const _Float16 *>(p.q) +
+                          ((int64_t)(q0 + r) * p.num_heads + h) * D + g * (D / 2);
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) qb[j] = q_ok ? load_half8(row + 8 * j) : half8{};
   }
@@ -91,52 +205,48 @@ prefill_kernel(const PrefillParams p) {
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t0 = 0; t0 < kv_end; t0 += kKeys) {
-    // Stage V^T of keys t0 .. t0+31 into LDS (zeros past the context).
-    __syncthreads();
-    for (int chunk = threadIdx.x; chunk < kKeys * (D / 8); chunk += kWaves * 64) {
-      const int key = chunk / (D / 8);
-      const int d0 = (chunk % (D / 8)) * 8;
-      const int t = t0 + key;
-      half8 v = {};
-      if (t < n) {
-        const int32_t phys = table[t / B];
-        if (phys >= 0 && phys < p.num_blocks)
-          v = load_half8(vh + (((int64_t)phys * p.num_heads + h) * B + t % B) * D + d0);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[(d0 + e) * kVtStride + key] = v[e];
-    }
+  // The table entries the workgroup needs, once, into LDS.
+  if (kLdsTable) {
+    const int nblk = (kv_end + B - 1) / B;      // at most kTabCache here
+    for (int j = threadIdx.x; j < nblk; j += kThreads) tab[j] = table[j];
+  }
+  // Drain the query and table loads here, once: memory counters retire in
+  // order, so a wait for the query fragments inside the loop would also
+  // wait for the next tile's loads issued just before it.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-    // S^T = K Q^T.  Lane row c holds key t0 + c.
+  TileLoads<D, B> next;
+  if (kv_end > 0) {
+    fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, 0, next);
+    store_tile<D, B>(next, lds, lds + L::kK);
+  }
+  __syncthreads();
+
+  int buf = 0;
+  for (int t0 = 0; t0 < kv_end; t0 += kKeys) {
+    const bool more = t0 + kKeys < kv_end;
+    if (more) fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, t0 + kKeys, next);
+    const _Float16 *ks = lds + buf * (L::kK + L::kV);
+    const _Float16 *vs = ks + L::kK;
+
+    // S^T = K Q^T.  A operand: key row c, head-dim half g.
     float16v s = {};
     {
-      const int t = t0 + c;
-      const _Float16 *krow = nullptr;
-      bool poison = false;
-      if (t < n) {
-        const int32_t phys = table[t / B];
-        if (phys >= 0 && phys < p.num_blocks)
-          krow = kh + (((int64_t)phys * p.num_heads + h) * B + t % B) * D + g * (D / 2);
-        else
-          poison = true;   // a table entry outside the pool: NaN for whoever sees it
-      }
+      const _Float16 *krow = ks + c * L::kRowK + g * (D / 2);
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) {
-        half8 a = {};
-        if (krow) a = load_half8(krow + 8 * j);
-        if (poison) a = half8{} + (_Float16)NAN;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[j], s, 0, 0, 0);
-      }
+      for (int j = 0; j < kSteps; ++j)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(load_half8(krow + 8 * j), qb[j], s, 0, 0, 0);
     }
 
-    // Online softmax for this lane's query over the tile's valid keys.
+    // Online softmax for this lane's query over the tile's visible keys.
     float tile_max = -INFINITY;
+    const bool full = t0 + kKeys - 1 <= n - m + qt * kQTile + w * kRows;  // no key past any query
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = t0 + (i / 4) * 8 + g * 4 + (i % 4);
       const float x = s[i] * p.scale_log2;
-      s[i] = key <= pos ? x : -INFINITY;
+      s[i] = (full || key <= pos) ? x : -INFINITY;
       tile_max = fmaxf(tile_max, s[i]);
     }
     tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
@@ -154,16 +264,17 @@ prefill_kernel(const PrefillParams p) {
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
     m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc_o[t] *= alpha;
 
-    __syncthreads();   // V^T staged
     // O^T += V^T P^T.  k-step jj covers keys 16jj .. 16jj+15 in the order
-    // the score registers hold them: slots e = 0..3 -> keys 16jj + 4g + e,
+    // the score registers hold them: slots 0..3 -> keys 16jj + 4g + e,
     // slots 4..7 -> keys 16jj + 8 + 4g + (e - 4).
+    if (__ballot(alpha != 1.f)) {   // the running max moved for some query
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const _Float16 *vrow = vt + (dt * 32 + c) * kVtStride;
+      const _Float16 *vrow = vs + (dt * 32 + c) * L::kRowV;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const half4 lo = *reinterpret_cast<const half4 *>(vrow + 16 * jj + 4 * g);
@@ -172,6 +283,13 @@ prefill_kernel(const PrefillParams p) {
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[jj], acc_o[dt], 0, 0, 0);
       }
     }
+
+    if (more) {
+      _Float16 *nk = lds + (buf ^ 1) * (L::kK + L::kV);
+      store_tile<D, B>(next, nk, nk + L::kK);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
 
   if (r >= m || q0 + r >= p.num_query_rows || r < 0) return;
@@ -190,17 +308,69 @@ prefill_kernel(const PrefillParams p) {
 }
 
 template <int D>
-hipError_t launch_prefill_d(const PrefillParams &p, int num_seqs, int block_size,
-                            int max_query_len, hipStream_t stream) {
-  const dim3 grid(p.num_heads, (max_query_len + kQTile - 1) / kQTile, num_seqs);
-  switch (block_size) {
-    case 8: prefill_kernel<D, 8><<<grid, kWaves * 64, 0, stream>>>(p); break;
-    case 16: prefill_kernel<D, 16><<<grid, kWaves * 64, 0, stream>>>(p); break;
-    case 32: prefill_kernel<D, 32><<<grid, kWaves * 64, 0, stream>>>(p); break;
-    case 64: prefill_kernel<D, 64><<<grid, kWaves * 64, 0, stream>>>(p); break;
-    default: return hipErrorInvalidValue;
+constexpr int lds_halves() {
+  return 2 * (Lds<D>::kK + Lds<D>::kV);
+}
+
+// Dispatch on whether the workgroup's table row fits its LDS copy (uniform
+// per workgroup).
+template <int D, int B>
+__device__ inline void prefill_dispatch(const PrefillParams &p, int h, int b, int qt,
+                                        _Float16 *lds,
+                                        __attribute__((address_space(3))) int32_t *tab) {
+  const int m = p.query_start[b + 1] - p.query_start[b];
+  const int n = min(max(p.context_lens[b], 0), p.max_context_len);
+  const int last_key = n - m + min(m, (qt + 1) * kQTile);   // kv_end when the chunk is valid
+  if ((last_key + B - 1) / B <= kTabCache)
+    prefill_item<D, B, true>(p, h, b, qt, lds, tab);
+  else
+    prefill_item<D, B, false>(p, h, b, qt, lds, tab);
+}
+
+// grid (heads, query tiles, sequences); tiles in descending order.
+template <int D, int B>
+__global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
+  __shared__ int32_t tab[kTabCache];
+  prefill_dispatch<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y, lds,
+                         (__attribute__((address_space(3))) int32_t *)tab);
+}
+
+// grid (heads, items): items = sequence << 16 | query tile, heaviest first.
+template <int D, int B>
+__global__ void __launch_bounds__(kThreads) prefill_listed_kernel(const PrefillParams p,
+                                                                  const WorkList items) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
+  __shared__ int32_t tab[kTabCache];
+  const uint32_t it = items.item[blockIdx.y];
+  prefill_dispatch<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), lds,
+                         (__attribute__((address_space(3))) int32_t *)tab);
+}
+
+template <int D, int B>
+hipError_t launch_db(const PrefillParams &p, int num_seqs, int max_query_len,
+                     const WorkList *items, hipStream_t stream) {
+  if (items) {
+    if (items->count > 0)
+      prefill_listed_kernel<D, B>
+          <<<dim3(p.num_heads, items->count), kThreads, 0, stream>>>(p, *items);
+  } else {
+    const dim3 grid(p.num_heads, (max_query_len + kQTile - 1) / kQTile, num_seqs);
+    prefill_kernel<D, B><<<grid, kThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillParams &p, int num_seqs, int block_size, int max_query_len,
+                    const WorkList *items, hipStream_t stream) {
+  switch (block_size) {
+    case 8: return launch_db<D, 8>(p, num_seqs, max_query_len, items, stream);
+    case 16: return launch_db<D, 16>(p, num_seqs, max_query_len, items, stream);
+    case 32: return launch_db<D, 32>(p, num_seqs, max_query_len, items, stream);
+    case 64: return launch_db<D, 64>(p, num_seqs, max_query_len, items, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -208,9 +378,9 @@ hipError_t launch_prefill_d(const PrefillParams &p, int num_seqs, int block_size
 int prefill_query_tile() { return kQTile; }
 
 hipError_t launch_prefill(const PrefillParams &p, int num_seqs, int head_dim, int block_size,
-                          int max_query_len, hipStream_t stream) {
-  if (head_dim == 128) return launch_prefill_d<128>(p, num_seqs, block_size, max_query_len, stream);
-  if (head_dim == 64) return launch_prefill_d<64>(p, num_seqs, block_size, max_query_len, stream);
+                          int max_query_len, const WorkList *items, hipStream_t stream) {
+  if (head_dim == 128) return launch_d<128>(p, num_seqs, block_size, max_query_len, items, stream);
+  if (head_dim == 64) return launch_d<64>(p, num_seqs, block_size, max_query_len, items, stream);
   return hipErrorInvalidValue;
 }
 

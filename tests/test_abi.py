@@ -148,6 +148,31 @@ def test_decode_rejects(pa, over, code):
     assert decode_call(pa.library(), **over) == code
 
 
+def prefill_call(lib, **over):
+    args = dict(out=OUT, q=Q, k_pool=KP, v_pool=VP, block_tables=TB, context_lens=CL,
+                query_start=CL, num_seqs=4, num_query_rows=40, num_heads=2, head_dim=64,
+                block_size=16, num_blocks=32, max_blocks_per_seq=4, max_context_len=50,
+                max_query_len=20, scale=0.125, dtype=0, host_query_start=None,
+                host_context_lens=None, stream=None)
+    args.update(over)
+    return lib.pa_prefill(*args.values())
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(query_start=None), -1),
+    (dict(block_tables=None), -1),
+    (dict(dtype=1), -3), (dict(head_dim=96), -3), (dict(block_size=4), -3),
+    (dict(max_query_len=51), -2), (dict(max_context_len=65, max_query_len=20), -2),
+    (dict(num_seqs=-1), -2), (dict(num_query_rows=-1), -2), (dict(scale=float("inf")), -2),
+    (dict(q=Q + 8), -2), (dict(query_start=CL + 2), -2), (dict(num_seqs=70000), -2),
+    (dict(num_seqs=0, out=None), 0), (dict(num_query_rows=0, q=None), 0),
+    (dict(max_query_len=0, out=None), 0),
+])
+def test_prefill_rejects(pa, over, code):
+    assert prefill_call(pa.library(), **over) == code
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
 def test_decode_empty_batch_is_ok_without_launch(pa):
     assert decode_call(pa.library(), num_seqs=0, out=None, q=None) == 0

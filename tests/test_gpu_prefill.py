@@ -28,7 +28,7 @@ def dev(a, device):
 
 
 def run_gpu(pa, wl, device, q=None, query_start=None, context_lens=None, tables=None,
-            max_query_len=None, k_pool=None):
+            max_query_len=None, k_pool=None, listed=False):
     q = wl.q if q is None else q
     qs = wl.query_start if query_start is None else query_start
     ctx = wl.context_lens if context_lens is None else context_lens
@@ -39,7 +39,9 @@ def run_gpu(pa, wl, device, q=None, query_start=None, context_lens=None, tables=
     pa.pa_prefill(out, dq, dev(wl.k_pool if k_pool is None else k_pool, device),
                   dev(wl.v_pool, device), dev(tables, device), dev(ctx, device), dev(qs, device),
                   float(wl.scale), max(int(np.max(ctx)) if len(ctx) else 0, 1),
-                  mq if max_query_len is None else max_query_len)
+                  mq if max_query_len is None else max_query_len,
+                  host_query_start=qs if listed else None,
+                  host_context_lens=ctx if listed else None)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -73,6 +75,21 @@ def test_prefill_matches_oracle(pa, oracle_lib, device, name):
     ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
                              wl.query_start, wl.scale)
     check(run_gpu(pa, wl, device), ref, name)
+
+
+@pytest.mark.parametrize("name", ["mix", "shared", "small-b8-d128", "small-b64-d128"])
+def test_prefill_listed_launch(pa, oracle_lib, device, name):
+    """With host copies of query_start and context_lens the library launches
+    the existing tiles heaviest first: same oracle parity, and bit for bit
+    the grid launch's output."""
+    announce(f"prefill listed launch {name}")
+    wl = CASES[name]()
+    listed = run_gpu(pa, wl, device, listed=True)
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(listed, ref, name)
+    grid = run_gpu(pa, wl, device)
+    assert np.array_equal(listed.view(np.uint16), grid.view(np.uint16))
 
 
 def test_prefill_edges(pa, oracle_lib, device):
@@ -137,7 +154,7 @@ def test_prefill_full_size_sampled(pa, oracle_lib, device, which):
     windows of rows checked against the oracle on truncated contexts."""
     announce(f"prefill full size {which}")
     wl = W.prefill_mix() if which == "mix" else W.prefill_shared()
-    got = run_gpu(pa, wl, device)
+    got = run_gpu(pa, wl, device, listed=True)
     rng = np.random.default_rng(17)
     for b, s, k in sampled_rows(wl, 6, rng):
         n, m = int(wl.context_lens[b]), int(wl.query_lens[b])
