@@ -78,6 +78,7 @@ struct TileLoads {
   half8 v[Lds<D>::kVPairs][2];
   bool kok[Lds<D>::kKChunks], kbad[Lds<D>::kKChunks];
   bool vok[Lds<D>::kVPairs][2];
+  bool all_ok;   // every key this wave loads comes from the pool (uniform per wave)
 };
 
 // Global -> registers for keys t0 .. t0+31; keys at or past `end` (the
@@ -119,12 +120,14 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
       vphys[u][s] = kLdsTable ? tab[j] : table[j];
     }
   }
+  bool all = true;
 #pragma unroll
   for (int u = 0; u < NK; ++u) {
     const bool in = kt[u] < end;
     const bool ok = in && kphys[u] >= 0 && kphys[u] < p.num_blocks;
     r.kok[u] = ok;
     r.kbad[u] = in && !ok;
+    all = all && ok;
     const int64_t row = ok ? ((int64_t)kphys[u] * p.num_heads + h) * B + kt[u] % B : 0;
     r.k[u] = load_half8(kh + row * D + kd[u]);
   }
@@ -134,9 +137,11 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
     for (int s = 0; s < 2; ++s) {
       const bool ok = vt[u][s] < end && vphys[u][s] >= 0 && vphys[u][s] < p.num_blocks;
       r.vok[u][s] = ok;
+      all = all && ok;
       const int64_t row = ok ? ((int64_t)vphys[u][s] * p.num_heads + h) * B + vt[u][s] % B : 0;
       r.v[u][s] = load_half8(vh + row * D + vd[u]);
     }
+  r.all_ok = __ballot(!all) == 0;   // uniform per wave
 }
 
 // Registers -> LDS buffers (K row-major, V transposed as key pairs).
@@ -147,8 +152,11 @@ __device__ inline void store_tile(const TileLoads<D, B> &r, _Float16 *ks, _Float
     const int chunk = threadIdx.x + u * kThreads;
     if (chunk < Lds<D>::kKUnits) {
       const int key = chunk / (D / 8), d0 = (chunk % (D / 8)) * 8;
-      half8 v = r.kok[u] ? r.k[u] : half8{};
-      if (r.kbad[u]) v = half8{} + (_Float16)NAN;   // NaN for every query that sees it
+      half8 v = r.k[u];
+      if (!r.all_ok) {
+        if (!r.kok[u]) v = half8{};
+        if (r.kbad[u]) v = half8{} + (_Float16)NAN;   // NaN for every query that sees it
+      }
       *reinterpret_cast<half8 *>(ks + key * Lds<D>::kRowK + d0) = v;
     }
   }
@@ -158,8 +166,11 @@ __device__ inline void store_tile(const TileLoads<D, B> &r, _Float16 *ks, _Float
     if (unit < Lds<D>::kVUnits) {
       const int kp = unit % (kKeys / 2), d0 = (unit / (kKeys / 2)) * 8;
       // word e = (key 2kp, key 2kp+1) at head-dim d0 + e
-      const half8 v0 = r.vok[u][0] ? r.v[u][0] : half8{};
-      const half8 v1 = r.vok[u][1] ? r.v[u][1] : half8{};
+      half8 v0 = r.v[u][0], v1 = r.v[u][1];
+      if (!r.all_ok) {
+        if (!r.vok[u][0]) v0 = half8{};
+        if (!r.vok[u][1]) v1 = half8{};
+      }
       const half16 z = __builtin_shufflevector(v0, v1, 0, 8, 1, 9, 2, 10, 3, 11,
                                                4, 12, 5, 13, 6, 14, 7, 15);
       const uint8v words = __builtin_bit_cast(uint8v, z);
@@ -189,6 +200,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   const int pos = n - m + r;                         // its position in the sequence
   const int last = min(m, (qt + 1) * kQTile) - 1;
   const int kv_end = bad_seq ? 0 : n - m + last + 1; // keys the workgroup needs
+  const int wave_pos0 = n - m + qt * kQTile + w * kRows;   // the wave's first query position
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
   constexpr int kSteps = D / 16;
@@ -240,16 +252,20 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     }
 
     // Online softmax for this lane's query over the tile's visible keys.
-    float tile_max = -INFINITY;
-    const bool full = t0 + kKeys - 1 <= n - m + qt * kQTile + w * kRows;  // no key past any query
+    // The maximum is taken on raw scores (the scale is positive) and the
+    // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
+    // Tiles wholly at or below every query of the wave skip the mask.
+    if (t0 + kKeys - 1 > wave_pos0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = t0 + (i / 4) * 8 + g * 4 + (i % 4);
-      const float x = s[i] * p.scale_log2;
-      s[i] = (full || key <= pos) ? x : -INFINITY;
-      tile_max = fmaxf(tile_max, s[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + (i / 4) * 8 + g * 4 + (i % 4);
+        if (key > pos) s[i] = -INFINITY;
+      }
     }
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+    float tile_max = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[i]);
+    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32)) * p.scale_log2;
     const float m_new = fmaxf(m_run, tile_max);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -257,7 +273,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     half8 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(s[i] - m_use);
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -m_use));
       psum += e;
       pb[i / 8][i % 8] = (_Float16)e;
     }
