@@ -20,7 +20,9 @@ threads) as a reported baseline, and checks sampled GPU rows against it.
 
 ``--workload generation`` instead times the multi-step decoding loop that
 the host block manager drives (parallel sampling with beam-like pruning at
-the same layer shape, every step over all L layers) and prints its own line.
+the same layer shape, every step over all L layers) and prints its own line;
+``--workload beam`` does the same for beam search with fork and prune at
+every step.
 ``--workload swap`` times block swapping between the device pool and a
 pinned host pool against the block size and prints its own line.
 ``--workload prefill`` times paged prefill attention (MFMA) on a full
@@ -296,7 +298,9 @@ def bench_generation(args):
     lognormal, median 300, clipped [1, 2048]) x 4 parallel samples sharing
     each prompt's blocks, 40 heads x head_dim 128, fp16, B = 16; before a
     step, with probability 1/4, one sample is pruned and another sample of
-    its prompt forked in its place.  A step = the manager's decisions and
+    its prompt forked in its place.  With --workload beam: 16 prompts x
+    beam width 4, every beam drawn again from its parents each step (pruned
+    beams freed, repeated parents forked).  A step = the manager's decisions and
     their upload (once), then for each of L layers: copy-on-write copies,
     KV write, paged decode.  Model GEMMs are not part of this path."""
     import torch
@@ -309,9 +313,16 @@ def bench_generation(args):
     L, K, Wm = args.layers, args.steps, args.warmup
     rng = np.random.default_rng(21)
     plens = W.lognormal_lengths(rng, 16)
-    g = W.generation(seed=21, dtype=W.F16, num_heads=40, head_dim=128, block_size=16,
-                     prompt_lens=tuple(int(x) for x in plens), samples=4, steps=Wm + K,
-                     churn=0.25)
+    beam = args.workload == "beam"
+    if beam:
+        g = W.beam_search(seed=21, dtype=W.F16, num_heads=40, head_dim=128, block_size=16,
+                          prompt_lens=tuple(int(x) for x in plens), width=4, steps=Wm + K)
+        label = "beam search 16 prompts x width 4"
+    else:
+        g = W.generation(seed=21, dtype=W.F16, num_heads=40, head_dim=128, block_size=16,
+                         prompt_lens=tuple(int(x) for x in plens), samples=4, steps=Wm + K,
+                         churn=0.25)
+        label = "parallel sampling 16 prompts x 4 samples"
     H, D, B = g.num_heads, g.head_dim, g.block_size
     shape = (g.num_blocks, H, B, D)
     pools = [tuple(torch.full(shape, float("nan"), dtype=torch.float16, device=device)
@@ -385,7 +396,7 @@ def bench_generation(args):
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded; lognormal prompt lengths, N(0,1) q/K/V)",
-        "config": {"workload": f"parallel sampling 16 prompts x 4 samples, OPT-13B-shaped "
+        "config": {"workload": f"{label}, OPT-13B-shaped "
                                f"attention, {L} layers per step",
                    "num_heads": H, "head_dim": D, "block_size": B, "layers": L,
                    "prompt_lens_sum": int(sum(plens)), "num_blocks": g.num_blocks},
@@ -396,6 +407,8 @@ def bench_generation(args):
         "layer_ms_mean": round(float(layer_ms.mean()), 5),
         "layer_attention_GBps": round(dec_bytes / (L * K) / (float(layer_ms.mean()) * 1e-3) / 1e9, 1),
         "cow_copies_per_step": round(copies / K, 3),
+        "forks_per_step": round(sum(len(g.steps[i].forks) for i in range(Wm, Wm + K)) / K, 3),
+        "prunes_per_step": round(sum(len(g.steps[i].frees) for i in range(Wm, Wm + K)) / K, 3),
         "blocks_in_use_final": blocks_used[-1],
         "blocks_if_private_final": private_need[-1],
     }
@@ -415,10 +428,11 @@ def main():
                     help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
-    ap.add_argument("--workload", choices=["decode", "generation", "swap", "prefill"],
+    ap.add_argument("--workload", choices=["decode", "generation", "beam", "swap", "prefill"],
                     default="decode",
                     help="decode: one layer's decode step (the default line); generation: the "
-                         "block-manager decoding loop over all layers; swap: block swap "
+                         "block-manager decoding loop over all layers (beam: the same with "
+                         "beam search forking and pruning every step); swap: block swap "
                          "device <-> pinned host against the block size; prefill: paged "
                          "prefill attention")
     args = ap.parse_args()
@@ -429,7 +443,7 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy()
-    if args.workload == "generation":
+    if args.workload in ("generation", "beam"):
         return bench_generation(args)
     if args.workload == "swap":
         return bench_swap(args)

@@ -11,6 +11,7 @@
 #include "pa.h"
 #include "pa_manager.h"
 #include "pa_kernels.h"
+#include "pa_prefill.h"
 
 namespace {
 

@@ -1,4 +1,6 @@
-"""Multi-step generation through the host block manager.
+"""Multi-step generation through the host block manager: parallel sampling
+with occasional pruning (workloads.generation) and beam search that forks
+and prunes every step (workloads.beam_search).
 
 CPU (no GPU): the manager's slots and copy pairs, executed by the oracle's
 copy/write and read by the oracle's decode, give at every step the dense
@@ -88,14 +90,21 @@ def M(pa):
     return manager
 
 
-@pytest.mark.parametrize("kw", [
-    dict(dtype=W.F32, num_heads=2, head_dim=16, block_size=4),
-    dict(dtype=W.F16, num_heads=2, head_dim=32, block_size=16),
-    dict(dtype=W.F32, num_heads=1, head_dim=8, block_size=1, steps=12),
-    dict(dtype=W.F16, num_heads=2, head_dim=16, block_size=8, churn=0.9, seed=5),
+@pytest.mark.parametrize("make,kw", [
+    ("generation", dict(dtype=W.F32, num_heads=2, head_dim=16, block_size=4)),
+    ("generation", dict(dtype=W.F16, num_heads=2, head_dim=32, block_size=16)),
+    ("generation", dict(dtype=W.F32, num_heads=1, head_dim=8, block_size=1, steps=12)),
+    ("generation", dict(dtype=W.F16, num_heads=2, head_dim=16, block_size=8, churn=0.9, seed=5)),
+    ("beam_search", dict(dtype=W.F32, num_heads=2, head_dim=16, block_size=4)),
+    ("beam_search", dict(dtype=W.F16, num_heads=2, head_dim=16, block_size=16, width=6,
+                         steps=40, spread=2.0, seed=3)),
+    ("beam_search", dict(dtype=W.F32, num_heads=1, head_dim=8, block_size=1, width=3, steps=10)),
 ])
-def test_managed_steps_equal_dense_attention(oracle_lib, M, kw):
-    g = W.generation(**kw)
+def test_managed_steps_equal_dense_attention(oracle_lib, M, make, kw):
+    """Also the beam-search workload: every step each request's beams are
+    drawn again from their parents, pruned beams freed, repeated parents
+    forked (the wywy.jp notes, WHERE beam search)."""
+    g = getattr(W, make)(**kw)
     record, _, _, m = run_oracle(oracle_lib, M, g)
     copies = sum(len(r[1]) for r in record)
     # with B > 1 forks share partly filled blocks, so copy-on-write happens;
@@ -107,18 +116,25 @@ def test_managed_steps_equal_dense_attention(oracle_lib, M, kw):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kw", [
-    dict(dtype=W.F16, num_heads=4, head_dim=128, block_size=16),
-    dict(dtype=W.F16, num_heads=4, head_dim=128, block_size=8, churn=0.6, seed=7, steps=40),
-    dict(dtype=W.F32, num_heads=2, head_dim=64, block_size=16, seed=9),
-    dict(dtype=W.F16, num_heads=8, head_dim=64, block_size=32, prompt_lens=(300, 1, 2, 31, 33),
-         samples=4, steps=20),
+@pytest.mark.parametrize("make,kw", [
+    ("generation", dict(dtype=W.F16, num_heads=4, head_dim=128, block_size=16)),
+    ("generation", dict(dtype=W.F16, num_heads=4, head_dim=128, block_size=8, churn=0.6, seed=7,
+                        steps=40)),
+    ("generation", dict(dtype=W.F32, num_heads=2, head_dim=64, block_size=16, seed=9)),
+    ("generation", dict(dtype=W.F16, num_heads=8, head_dim=64, block_size=32,
+                        prompt_lens=(300, 1, 2, 31, 33), samples=4, steps=20)),
+    ("beam_search", dict(dtype=W.F16, num_heads=4, head_dim=128, block_size=16, width=4,
+                         steps=48)),
+    ("beam_search", dict(dtype=W.F16, num_heads=4, head_dim=64, block_size=8, width=8,
+                         steps=40, spread=3.0, seed=4)),
+    ("beam_search", dict(dtype=W.F32, num_heads=2, head_dim=128, block_size=32, width=5,
+                         prompt_lens=(200, 17, 64), steps=30, seed=6)),
 ])
-def test_decode_stepper_matches_oracle(oracle_lib, M, pa, device, kw):
+def test_decode_stepper_matches_oracle(oracle_lib, M, pa, device, make, kw):
     import torch
-    print(f"[gpu] step loop {kw}", flush=True)
+    print(f"[gpu] step loop {make} {kw}", flush=True)
     sys.stdout.flush()
-    g = W.generation(**kw)
+    g = getattr(W, make)(**kw)
     record, k_ref, v_ref, _ = run_oracle(oracle_lib, M, g, dense=False)
     tdt = torch.float16 if g.dtype == W.F16 else torch.float32
     shape = (g.num_blocks, g.num_heads, g.block_size, g.head_dim)

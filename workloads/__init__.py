@@ -568,6 +568,71 @@ def generation(seed=11, dtype=F16, num_heads=4, head_dim=128, block_size=16,
                       prompt_keys=prompt_keys, prompt_values=prompt_values, steps=out)
 
 
+def beam_search(seed=17, dtype=F16, num_heads=4, head_dim=128, block_size=16,
+                prompt_lens=(37, 5, 64, 100, 1), width=4, steps=24, spread=1.0):
+    """Beam search with fork and prune every step.
+
+    Each prompt is written, then forked into ``width`` beams sharing its
+    blocks.  Before every later step each request draws ``width`` parents
+    from its ``width`` live beams, with replacement, with probabilities
+    softmax(spread * N(0,1)) (a stand-in for the candidates' scores: no
+    model is run).  A beam drawn by no one is pruned (freed); a beam drawn
+    c times continues as one candidate and is forked c - 1 times, so the
+    candidates share its blocks, and the partly filled last block is copied
+    when they append (the wywy.jp notes, WHERE beam search: candidates share
+    blocks, a pruned candidate's blocks lose a reference, copy-on-write on
+    the shared partial block).  Every live beam then appends one token.
+    """
+    rng = np.random.default_rng(seed)
+    dt = NP_DTYPES[dtype]
+    H, D, B = num_heads, head_dim, block_size
+    P = len(prompt_lens)
+    prompt_keys = [_normal(rng, (int(L), H, D), dt) for L in prompt_lens]
+    prompt_values = [_normal(rng, (int(L), H, D), dt) for L in prompt_lens]
+    beams = [[p] for p in range(P)]           # per request, its live beam ids
+    next_id = P
+    length = {p: int(L) for p, L in enumerate(prompt_lens)}
+    peak_blocks = 0
+    out = []
+    for t in range(steps):
+        frees, forks = [], []
+        for r in range(P):
+            cur = beams[r]
+            if t == 0:
+                parents = [cur[0]] * width
+            else:
+                logits = spread * rng.standard_normal(len(cur))
+                prob = np.exp(logits - logits.max())
+                prob /= prob.sum()
+                parents = [cur[i] for i in rng.choice(len(cur), size=width, p=prob)]
+            counts = {b: parents.count(b) for b in cur}
+            new = []
+            for b in cur:
+                if counts[b] == 0:
+                    frees.append(b)
+                    continue
+                new.append(b)
+                for _ in range(counts[b] - 1):
+                    forks.append((b, next_id))
+                    length[next_id] = length[b]
+                    new.append(next_id)
+                    next_id += 1
+            beams[r] = new
+        live = [b for r in range(P) for b in beams[r]]
+        n = len(live)
+        out.append(GenStep(frees=frees, forks=forks, seqs=live,
+                           key=_normal(rng, (n, H, D), dt), value=_normal(rng, (n, H, D), dt),
+                           q=_normal(rng, (n, H, D), dt)))
+        for b in live:
+            length[b] += 1
+        peak_blocks = max(peak_blocks, sum(_blocks_for(length[b], B) for b in live))
+    max_len = max(length.values())
+    return Generation(name="beam-search", seed=seed, dtype=dtype, num_heads=H, head_dim=D,
+                      block_size=B, num_blocks=peak_blocks + P + 4,
+                      max_blocks=_blocks_for(max_len, B), scale=np.float32(1.0 / math.sqrt(D)),
+                      prompt_keys=prompt_keys, prompt_values=prompt_values, steps=out)
+
+
 # ---------------------------------------------------------------------------
 # Generation under memory pressure: groups of parallel samples that outgrow
 # the GPU pool, so that some group must be preempted (and swapped out) for
