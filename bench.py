@@ -424,6 +424,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="layer pools to rotate over")
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-step", action="store_true",
+                    help="pa_write_kv then pa_decode (two launches) instead of the fused "
+                         "pa_decode_append")
     ap.add_argument("--no-host-lengths", action="store_true",
                     help="do not pass host-side context lengths to pa_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -477,17 +480,22 @@ def main():
     merges = -(-maxctx // part) > 1
     kernel = ("decode_listed_kernel" if host_ctx is not None else "decode_kernel") + \
         f"<{'f16' if wl.dtype == W.F16 else 'f32'},{D},{B},8>" + \
-        (" + merge_kernel" if merges else "")
+        (" + merge_kernel" if merges else "") + \
+        ("" if args.split_step else " (fused append: pa_decode_append)")
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
         k, v = pools[i % L]
         pa.pa_copy_blocks(k, v, copies)              # no pairs in this workload: no launch
-        pa.pa_write_kv(new_k, new_v, k, v, slots)
         if ev is not None:
             ev[0].record(stream)
-        pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws,
-                     host_context_lens=host_ctx)
+        if args.split_step:
+            pa.pa_write_kv(new_k, new_v, k, v, slots)
+            pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws,
+                         host_context_lens=host_ctx)
+        else:
+            pa.pa_decode_append(out, q, new_k, new_v, k, v, tables, ctx, slots, scale, maxctx,
+                                args.partition, ws, host_context_lens=host_ctx)
         if ev is not None:
             ev[1].record(stream)
 
@@ -510,18 +518,20 @@ def main():
     ms_per_step = total_ms / K
 
     decode_bytes = wl.algorithmic_bytes()
-    write_bytes = 4 * N * H * D * wl.elem_bytes     # read key + value, write both pools
-    step_bytes = decode_bytes + write_bytes
+    # the step's necessary traffic: every context token's K and V once (the
+    # new one from its input row), q, out, and the new rows stored once
+    step_bytes = decode_bytes + 2 * N * H * D * wl.elem_bytes
+    # the timed launch: the fused kernel does the whole step; the split form
+    # times pa_decode alone
+    call_bytes = decode_bytes if args.split_step else step_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_mean = float(dec_ms.mean())
-    achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
-    traffic = measured_traffic()
+    achieved = call_bytes / (dec_mean * 1e-3) / 1e9
+    traffic = None if args.split_step else measured_traffic()
 
     # Output of layer 0 for the parity sample and the CPU baseline.
     k0, v0 = pools[0]
-    pa.pa_write_kv(new_k, new_v, k0, v0, slots)
-    pa.pa_decode(out, q, k0, v0, tables, ctx, scale, maxctx, args.partition, ws,
-                 host_context_lens=host_ctx)
+    step(0)                                      # the timed call, on layer 0's pools
     torch.cuda.synchronize()
     gpu_out = out.cpu().numpy().astype(np.float64)
     if not np.isfinite(gpu_out).all():
@@ -561,7 +571,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded; lognormal context lengths, N(0,1) q/K/V, scattered blocks)",
         "config": {
-            "workload": "OPT-13B-shaped single-layer decode step (write_kv + paged decode)",
+            "workload": "OPT-13B-shaped single-layer decode step (new-token store + paged decode)",
             "num_seqs": N, "num_heads": H, "head_dim": D, "block_size": B,
             "context_lens": "lognormal median 300 sigma 0.9 clipped [1,2048]",
             "sum_context": int(wl.context_lens.sum()), "max_context": maxctx,
@@ -572,6 +582,7 @@ def main():
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_bytes_per_call": decode_bytes,
+        "timed_call_bytes": call_bytes,
         "decode_ms_mean": round(dec_mean, 5),
         "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_ms, [10, 50, 90])],
         "roofline": {

@@ -193,6 +193,34 @@ int pa_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_mapping,
                    int num_blocks, int dtype, void *stream);
 
 /*
+ * One decoding step fused: store every sequence's new token and attend over
+ * the context that includes it.  The same result, bit for bit, as
+ * pa_write_kv(new_key, new_value, k_pool, v_pool, slot_mapping, num_seqs,
+ * ...) followed by pa_decode(out, q, ...): each step creates K/V for the
+ * new token only and stores it at the next free position of the sequence's
+ * last block (the wywy.jp notes, Keyword "autoregressive generation phase"
+ * and "KV cache manager"), and the query of that step attends over the
+ * whole context, the new token included.  One launch instead of two, and
+ * the new rows are read once, from new_key / new_value.
+ *
+ * new_key, new_value: [num_seqs][num_heads][head_dim], 16-byte aligned;
+ * slot_mapping: int64 [num_seqs], the slot (block * block_size + offset) of
+ * sequence b's new token, which must be the position context_lens[b] - 1
+ * under its block table (a slot outside the pool is not written, as in
+ * pa_write_kv; the attention still uses the new row for that position).
+ * Every other argument, the workspace and the errors are those of
+ * pa_decode.  No other sequence of the call may read the new token's slot
+ * (copy-on-write guarantees it: the block written is private).
+ */
+int pa_decode_append(void *out, const void *q, const void *new_key, const void *new_value,
+                     void *k_pool, void *v_pool, const int32_t *block_tables,
+                     const int32_t *context_lens, const int64_t *slot_mapping, int num_seqs,
+                     int num_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+                     int partition_size, const int32_t *host_context_lens, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * Paged prefill attention (the prompt phase).  Source: the PagedAttention
  * pages -- the wywy.jp notes, Keyword "prompt phase" (all prompt tokens are
  * known, so they are processed together, matrix-matrix) and WHERE, shared

@@ -7,6 +7,11 @@ carry the C names:
 
 * :func:`pa_decode` -- single-query decode attention over block pools
   addressed through per-sequence block tables,
+* :func:`pa_decode_append` -- one fused step: store each new token's K/V and
+  decode over the context that includes it,
+* :func:`pa_prefill` -- causal attention of a chunk of query tokens per
+  sequence over its paged context (the prompt phase),
+* :func:`pa_swap_blocks` -- whole blocks between device and pinned host pools,
 * :func:`pa_write_kv` -- store the new tokens' K/V rows in their slots,
 * :func:`pa_copy_blocks` -- copy-on-write copy of whole physical blocks,
 * :func:`pa_decode_workspace_bytes`, :func:`pa_decode_partition_size`,
@@ -40,7 +45,7 @@ def default_partition(max_context_len: int) -> int:
     return PA_LONG_PARTITION if max_context_len > PA_LONG_CONTEXT else PA_DEFAULT_PARTITION
 
 # Every symbol include/pa.h and include/pa_manager.h declare.
-EXPORTS = ("pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
+EXPORTS = ("pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
            "pa_copy_blocks", "pa_swap_blocks", "pa_prefill", "pa_status_string", "pa_last_error",
            "pa_manager_create", "pa_manager_destroy", "pa_manager_add", "pa_manager_fork",
            "pa_manager_append", "pa_manager_free", "pa_manager_tables", "pa_manager_num_free",
@@ -87,6 +92,9 @@ def library() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                               f32, i32, i32, vp, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, i32, vp, vp, sz, vp]
+    lib.pa_decode_append.restype = i32
     lib.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_bytes.restype = sz
     lib.pa_decode_partition_size.argtypes = [vp, i32, i32, i32, i32, i32, sz]
@@ -185,18 +193,8 @@ def new_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None, host_context_lens=None):
-    """out[N][H][D] = paged decode attention of q[N][H][D] over the pools.
-
-    k_pool/v_pool: [num_blocks][H][block_size][D]; block_tables int32
-    [N][max_blocks_per_seq]; context_lens int32 [N]; max_context_len: host
-    int >= every context length; workspace: from :func:`new_workspace`;
-    host_context_lens: optional host copy of context_lens (numpy int32 or a
-    sequence of ints), used only to plan the launch.
-    """
+def _decode_common(q, out, k_pool, v_pool, block_tables, context_lens, host_context_lens):
     import numpy as np
-    import torch
     host = None
     if host_context_lens is not None:
         host = np.ascontiguousarray(host_context_lens, dtype=np.int32)
@@ -212,6 +210,22 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
         raise PAError("q and pools must share one element type")
     if block_tables.dim() != 2 or block_tables.shape[0] != N or tuple(context_lens.shape) != (N,):
         raise PAError("block_tables / context_lens do not match the batch")
+    return host, (N, H, D, B, NB)
+
+
+def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_context_len,
+              partition_size=0, workspace=None, stream=None, host_context_lens=None):
+    """out[N][H][D] = paged decode attention of q[N][H][D] over the pools.
+
+    k_pool/v_pool: [num_blocks][H][block_size][D]; block_tables int32
+    [N][max_blocks_per_seq]; context_lens int32 [N]; max_context_len: host
+    int >= every context length; workspace: from :func:`new_workspace`;
+    host_context_lens: optional host copy of context_lens (numpy int32 or a
+    sequence of ints), used only to plan the launch.
+    """
+    import torch
+    host, (N, H, D, B, NB) = _decode_common(q, out, k_pool, v_pool, block_tables, context_lens,
+                                            host_context_lens)
     ws_ptr = _dev(workspace, "workspace", torch.uint8)
     ws_bytes = workspace.numel() if workspace is not None else 0
     rc = library().pa_decode(
@@ -221,6 +235,35 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
         int(partition_size), None if host is None else host.ctypes.data, ws_ptr, ws_bytes,
         _stream(stream))
     _check(rc, "pa_decode")
+    return out
+
+
+def pa_decode_append(out, q, new_key, new_value, k_pool, v_pool, block_tables, context_lens,
+                     slot_mapping, scale, max_context_len, partition_size=0, workspace=None,
+                     stream=None, host_context_lens=None):
+    """One fused decoding step: store new_key/new_value [N][H][D] at
+    slot_mapping (int64 [N], the slot of each sequence's position
+    context_lens - 1) and attend q over every context, the new token
+    included.  Bit for bit pa_write_kv followed by pa_decode."""
+    import torch
+    host, (N, H, D, B, NB) = _decode_common(q, out, k_pool, v_pool, block_tables, context_lens,
+                                            host_context_lens)
+    for t, name in ((new_key, "new_key"), (new_value, "new_value")):
+        if tuple(t.shape) != (N, H, D) or t.dtype != q.dtype:
+            raise PAError(f"{name} must match q in shape and type")
+    if tuple(slot_mapping.shape) != (N,):
+        raise PAError("slot_mapping must have one entry per sequence")
+    ws_ptr = _dev(workspace, "workspace", torch.uint8)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    rc = library().pa_decode_append(
+        _dev(out, "out"), _dev(q, "q"), _dev(new_key, "new_key"), _dev(new_value, "new_value"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(slot_mapping, "slot_mapping", torch.int64),
+        N, H, D, B, NB, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
+        int(partition_size), None if host is None else host.ctypes.data, ws_ptr, ws_bytes,
+        _stream(stream))
+    _check(rc, "pa_decode_append")
     return out
 
 

@@ -329,12 +329,15 @@ int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int
   return part;
 }
 
-int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
-              const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
-              int num_heads, int head_dim, int block_size, int num_blocks,
-              int max_blocks_per_seq, int max_context_len, float scale, int dtype,
-              int partition_size, const int32_t *host_context_lens, void *workspace,
-              size_t workspace_bytes, void *stream) {
+// pa_decode and pa_decode_append: the append arguments are all null for a
+// plain decode.
+static int decode_impl(const char *what, void *out, const void *q, const void *new_key,
+                       const void *new_value, const void *k_pool, const void *v_pool,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int64_t *slot_mapping, int num_seqs, int num_heads, int head_dim,
+                       int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                       float scale, int dtype, int partition_size, const int32_t *host_context_lens,
+                       void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
   int part = effective_partition(partition_size, max_context_len);
@@ -348,6 +351,12 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return PA_ERR_SHAPE;
+  const bool append = new_key || new_value || slot_mapping;
+  if (append) {
+    if (!new_key || !new_value || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned16(new_key) || !aligned16(new_value) || ((uintptr_t)slot_mapping & 7u))
+      return PA_ERR_SHAPE;
+  }
   if (host_context_lens && partition_size == 0)
     part = plan_partition(host_context_lens, num_seqs, num_heads, head_dim, max_context_len,
                           workspace_bytes, workspace != nullptr);
@@ -366,6 +375,9 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   p.partition_size = part;
   p.num_partitions = num_partitions(max_context_len, part);
   p.scale_log2 = scale * 1.44269504088896340736f;
+  p.new_key = new_key;
+  p.new_value = new_value;
+  p.slot_mapping = slot_mapping;
   if (p.num_partitions > 1) {
     const pa::WorkspaceLayout w =
         pa::decode_workspace_layout(num_seqs, num_heads, head_dim, p.num_partitions);
@@ -378,15 +390,41 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
   if (host_context_lens) {
     pa::WorkList items, merge_rows;
     if (plan_work(host_context_lens, num_seqs, max_context_len, part, &items, &merge_rows))
-      return launch_checked("pa_decode", [&] {
+      return launch_checked(what, [&] {
         return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, &items, &merge_rows,
                                  static_cast<hipStream_t>(stream));
       });
   }
-  return launch_checked("pa_decode", [&] {
+  return launch_checked(what, [&] {
     return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr,
                              static_cast<hipStream_t>(stream));
   });
+}
+
+int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
+              const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+              int num_heads, int head_dim, int block_size, int num_blocks,
+              int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+              int partition_size, const int32_t *host_context_lens, void *workspace,
+              size_t workspace_bytes, void *stream) {
+  return decode_impl("pa_decode", out, q, nullptr, nullptr, k_pool, v_pool, block_tables,
+                     context_lens, nullptr, num_seqs, num_heads, head_dim, block_size,
+                     num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, host_context_lens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append(void *out, const void *q, const void *new_key, const void *new_value,
+                     void *k_pool, void *v_pool, const int32_t *block_tables,
+                     const int32_t *context_lens, const int64_t *slot_mapping, int num_seqs,
+                     int num_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+                     int partition_size, const int32_t *host_context_lens, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  if (num_seqs > 0 && (!new_key || !new_value || !slot_mapping)) return PA_ERR_NULL;
+  return decode_impl("pa_decode_append", out, q, new_key, new_value, k_pool, v_pool,
+                     block_tables, context_lens, slot_mapping, num_seqs, num_heads, head_dim,
+                     block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, host_context_lens, workspace, workspace_bytes, stream);
 }
 
 int pa_write_kv(const void *key, const void *value, void *k_pool, void *v_pool,

@@ -167,7 +167,7 @@ struct ItemShared {
 // (max, sum, unnormalised output) for the merge pass.
 template <typename T, int D, int B, int W>
 __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T, D, W> &sh,
-                                             int b, int h, int part, int ctx) {
+                                             int b, int h, int part, int ctx, bool append) {
   using G = Geometry<T, D>;
   constexpr int kStates = ItemShared<T, D, W>::kStates;
   constexpr int kLPT = G::kLanesPerToken;
@@ -199,6 +199,13 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   const char *vbase = reinterpret_cast<const char *>(p.v_pool) + lane_off;
   const unsigned num_blocks = (unsigned)p.num_blocks;
   bool bad = false;
+  // Fused append: the token at position ctx - 1 comes from the new rows,
+  // not from the pool (which this workgroup is writing it to).
+  const int last = ctx - 1;
+  const char *nk = append ? reinterpret_cast<const char *>(p.new_key) + row * D * sizeof(T)
+                          : nullptr;
+  const char *nv = append ? reinterpret_cast<const char *>(p.new_value) + row * D * sizeof(T)
+                          : nullptr;
 
   // Load the 16-token tile starting at logical token ts.  With kCheck,
   // groups at or past tok_end are not loaded (their table entries may not
@@ -225,6 +232,13 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
         for (int k = 0; k < G::kChunksPerLane; ++k) {
           tile.k[g][k] = load_stream(kbase + boff + k * kLPT * 16);
           tile.v[g][k] = load_stream(vbase + boff + k * kLPT * 16);
+        }
+        if (append && ts <= last && last < ts + G::kTile && gs + trow == last) {
+#pragma unroll
+          for (int k = 0; k < G::kChunksPerLane; ++k) {
+            tile.k[g][k] = load_chunk(nk + (col + k * kLPT) * 16);
+            tile.v[g][k] = load_chunk(nv + (col + k * kLPT) * 16);
+          }
         }
       } else {
 #pragma unroll
@@ -396,11 +410,38 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
 // Workgroup for head h of sequence b, partition `part`: clamps the context
 // from the device array, writes a zero row for an empty context (partition
 // 0 only) and leaves at once when the partition holds no token.
+// Fused append: store the new token's K and V rows of (b, h) at its slot
+// (slots outside the pool are skipped, as pa_write_kv does).
+template <typename T, int D, int B, int W>
+__device__ __forceinline__ void store_new_token(const DecodeParams &p, int b, int h) {
+  const int64_t slot = p.slot_mapping[b];
+  if (slot < 0 || slot >= (int64_t)p.num_blocks * B) return;
+  constexpr int kC = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  const int64_t blk = slot / B;
+  const int off = (int)(slot - blk * B);
+  const size_t src = ((size_t)b * p.num_heads + h) * kC;
+  const size_t dst = (((size_t)blk * p.num_heads + h) * B + off) * kC;
+  for (int c = threadIdx.x; c < 2 * kC; c += 64 * W) {
+    if (c < kC)
+      reinterpret_cast<uint4 *>(const_cast<void *>(p.k_pool))[dst + c] =
+          reinterpret_cast<const uint4 *>(p.new_key)[src + c];
+    else
+      reinterpret_cast<uint4 *>(const_cast<void *>(p.v_pool))[dst + c - kC] =
+          reinterpret_cast<const uint4 *>(p.new_value)[src + c - kC];
+  }
+}
+
 template <typename T, int D, int B, int W>
 __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
                                            int b, int part) {
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
+  // With a fused append the item that owns the last token (partition 0 for
+  // an empty context) also stores the new rows; no other item of the launch
+  // reads that slot.
+  const int n_parts = (ctx + p.partition_size - 1) / p.partition_size;
+  const bool append = p.new_key != nullptr && part == (n_parts > 0 ? n_parts - 1 : 0);
+  if (append) store_new_token<T, D, B, W>(p, b, h);
   if (ctx == 0) {
     if (part == 0) {
       T *out_row = reinterpret_cast<T *>(p.out) + ((size_t)b * p.num_heads + h) * D;
@@ -409,7 +450,7 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
     return;
   }
   if (part * p.partition_size >= ctx) return;
-  process_item<T, D, B, W>(p, sh, b, h, part, ctx);
+  process_item<T, D, B, W>(p, sh, b, h, part, ctx, append);
 }
 
 // One workgroup per (head, sequence, partition); the hardware dispatcher

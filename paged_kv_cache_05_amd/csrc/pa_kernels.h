@@ -25,6 +25,12 @@ struct DecodeParams {
   float scale_log2;     // scale * log2(e): scores are kept in base 2
   float2 *part_ml;      // [num_seqs * num_heads][num_partitions] (max, sum)
   float *part_o;        // [num_seqs * num_heads][num_partitions][head_dim]
+  // Fused append (all null for a plain decode): the new token of sequence b
+  // (rows [b][h][:] of new_key / new_value) is stored at slot_mapping[b] and
+  // is the token at position context_lens[b] - 1 of the attention.
+  const void *new_key;
+  const void *new_value;
+  const int64_t *slot_mapping;
 };
 
 // Workspace carve-up shared by the size query and the launch.

@@ -6,8 +6,8 @@ of a shared last block).  :class:`DecodeStepper` runs one decoding step of a
 batch the way the PagedAttention pages describe it: the manager reserves
 each sequence's next slot (a fresh block when the last one is full, a
 private copy when it is shared), then the GPU copies the shared blocks
-(``pa_copy_blocks``), stores the new tokens' K/V (``pa_write_kv``) and
-attends over the whole context (``pa_decode``).  Argument marshalling and
+(``pa_copy_blocks``), then stores the new tokens' K/V and attends over the
+whole context in one launch (``pa_decode_append``).  Argument marshalling and
 bookkeeping only; all device work runs in the HIP kernels.
 """
 from __future__ import annotations
@@ -17,8 +17,8 @@ import time
 
 import numpy as np
 
-from . import PAError, library, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, \
-    pa_status_string, pa_swap_blocks, pa_write_kv
+from . import PAError, library, pa_copy_blocks, pa_decode_append, pa_decode_workspace_bytes, \
+    pa_status_string, pa_swap_blocks
 
 PA_ERR_NO_SEQUENCE = -6
 PA_ERR_EXISTS = -7
@@ -189,8 +189,8 @@ class DecodeStepper:
     manager.num_host_blocks blocks) is the swap space.  :meth:`plan` makes
     the step's host decisions and uploads them with one host-to-device copy
     from pinned memory; :meth:`layer` runs the step's device work on one
-    layer: copy-on-write copies (pa_copy_blocks), the new token's K/V
-    (pa_write_kv), decode attention (pa_decode).  :meth:`swap_out` and
+    layer: copy-on-write copies (pa_copy_blocks), then the new tokens' K/V
+    and the decode attention in one launch (pa_decode_append).  :meth:`swap_out` and
     :meth:`swap_in` move a preempted group's blocks to the swap space and
     back, on every layer (pa_swap_blocks).  All device work goes to torch's
     current stream, so a swap-out's copies finish before the freed blocks
@@ -272,10 +272,13 @@ class DecodeStepper:
 
     def plan(self, seqs) -> StepPlan:
         """Reserve every sequence's next slot (allocation and copy-on-write
-        decisions), build the tables and upload them."""
+        decisions), build the tables and upload them.  Each sequence appears
+        at most once: a step adds one token per sequence."""
         t = time.perf_counter()
         p = StepPlan()
         p.seqs = list(seqs)
+        if len(set(p.seqs)) != len(p.seqs):
+            raise PAError("a decoding step lists each sequence once")
         p.slots, p.pairs = self.manager.append(p.seqs)
         p.tables, p.context_lens = self.manager.tables(p.seqs, self.max_blocks)
         p.max_context_len = int(p.context_lens.max()) if len(p.seqs) else 0
@@ -285,17 +288,19 @@ class DecodeStepper:
         return p
 
     def layer(self, plan: StepPlan, layer, new_key, new_value, q, scale, out=None):
-        """The step's device work on one layer's pools; returns out [n][H][D]."""
+        """The step's device work on one layer's pools: the copy-on-write
+        copies, then one fused launch that stores the new tokens and decodes
+        (pa_decode_append); returns out [n][H][D]."""
         k, v = self.pools[layer]
         if len(plan.pairs):
             pa_copy_blocks(k, v, plan.d_pairs)
-        pa_write_kv(new_key, new_value, k, v, plan.d_slots)
         if out is None:
             out = self._torch.empty_like(q)
         n, H, D = q.shape
         ws = self._workspace(n, H, D, plan.max_context_len)
-        pa_decode(out, q, k, v, plan.d_tables, plan.d_context_lens, scale, plan.max_context_len,
-                  self.partition_size, ws, host_context_lens=plan.context_lens)
+        pa_decode_append(out, q, new_key, new_value, k, v, plan.d_tables, plan.d_context_lens,
+                         plan.d_slots, scale, plan.max_context_len, self.partition_size, ws,
+                         host_context_lens=plan.context_lens)
         return out
 
     def _swap(self, pairs, out):

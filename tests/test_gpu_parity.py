@@ -420,3 +420,85 @@ def test_pending_runtime_error_is_not_taken_for_the_launch(pa, oracle_lib, devic
     ref_k, ref_v = wl.k_pool_pre.copy(), wl.v_pool_pre.copy()
     oracle_lib.write_kv(wl.new_key, wl.new_value, ref_k, ref_v, wl.slot_mapping)
     assert np.array_equal(tbits(k), bits(ref_k)) and np.array_equal(tbits(v), bits(ref_v))
+
+
+# ---------------------------------------------------------------------------
+# pa_decode_append: the fused step, bit for bit pa_write_kv + pa_decode
+# ---------------------------------------------------------------------------
+
+def fused_and_split(pa, wl, device, partition_size=0, host=False, ctx=None, slots=None):
+    """(fused pools, fused out, split pools, split out) after the step's
+    copies, from the same pools before the step."""
+    ctx = wl.context_lens if ctx is None else ctx
+    slots = wl.slot_mapping if slots is None else slots
+    N, H, D = wl.q.shape
+    maxctx = max(int(np.max(ctx)), 1)
+    host_ctx = ctx if host else None
+    res = []
+    for fused in (True, False):
+        k, v = dev(wl.k_pool_pre, device), dev(wl.v_pool_pre, device)
+        if len(wl.block_mapping):
+            pa.pa_copy_blocks(k, v, dev(wl.block_mapping, device))
+        q, out = dev(wl.q, device), torch.full((N, H, D), float("nan"), device=device,
+                                                dtype=k.dtype)
+        ws = pa.new_workspace(N, H, D, maxctx, partition_size or 256, device=device)
+        args = (dev(wl.block_tables, device), dev(ctx, device))
+        nk, nv, sl = dev(wl.new_key, device), dev(wl.new_value, device), dev(slots, device)
+        if fused:
+            pa.pa_decode_append(out, q, nk, nv, k, v, *args, sl, float(wl.scale), maxctx,
+                                partition_size, ws, host_context_lens=host_ctx)
+        else:
+            pa.pa_write_kv(nk, nv, k, v, sl)
+            pa.pa_decode(out, q, k, v, *args, float(wl.scale), maxctx, partition_size, ws,
+                         host_context_lens=host_ctx)
+        torch.cuda.synchronize()
+        res += [(tbits(k), tbits(v)), tbits(out)]
+    return res
+
+
+@pytest.mark.parametrize("config,kw", [(1, {}), (2, {}), (3, {"block_size": 8}),
+                                       (3, {"block_size": 64})],
+                         ids=["cfg1", "cfg2", "cfg3-b8", "cfg3-b64"])
+@pytest.mark.parametrize("part,host", [(0, False), (0, True), (64, False), (64, True), (16, True)])
+def test_decode_append_equals_write_then_decode(pa, oracle_lib, device, config, kw, part, host):
+    """The fused step gives the same pools and the same outputs, bit for
+    bit, as the write followed by the decode -- with the new token in a
+    split partition (64, 16) and in either launch form."""
+    wl = workload(config, **kw)
+    announce(f"decode_append {wl.name} part={part} host={host}")
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, part, host)
+    assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    assert np.array_equal(fo, so)
+    if part == 0 and not host:
+        ok, ov = step_on_oracle(oracle_lib, wl)
+        assert np.array_equal(fk, bits(ok)) and np.array_equal(fv, bits(ov))
+        assert_close(fo.view(wl.q.dtype), oracle_decode(oracle_lib, wl, ok, ov), wl.dtype,
+                     "fused vs oracle")
+
+
+def test_decode_append_empty_context_still_writes(pa, device):
+    """A sequence with context 0 gets a zero row and its new token is still
+    stored (as pa_write_kv would)."""
+    announce("decode_append empty context")
+    wl = workload(1)
+    ctx = wl.context_lens.copy()
+    ctx[0] = 0
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=True, ctx=ctx)
+    assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    assert np.array_equal(fo, so)
+    assert not np.any(fo[0].view(wl.q.dtype))
+
+
+def test_decode_append_skips_slots_outside_pool(pa, device):
+    """A slot outside the pool is not written; the attention still uses the
+    new row for the last position, which equals the normal step's output."""
+    announce("decode_append slot outside pool")
+    wl = workload(1)
+    slots = wl.slot_mapping.copy()
+    slots[2] = -1
+    (fk, fv), fo, _, _ = fused_and_split(pa, wl, device, slots=slots)
+    _, normal, _, _ = fused_and_split(pa, wl, device)
+    before_k = tbits(dev(wl.k_pool_pre, device))
+    blk, off = divmod(int(wl.slot_mapping[2]), wl.block_size)
+    assert np.array_equal(fk[blk, :, off], before_k[blk, :, off])   # not written
+    assert np.array_equal(fo, normal)
