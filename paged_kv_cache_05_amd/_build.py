@@ -17,8 +17,12 @@ SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_
 LIBRARY = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-# Packed fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are disabled for all device code.  MFMA results
+# stay in arch VGPRs (the prefill kernel's accumulators are rescaled by VALU
+# code; in AGPRs every such use costs a move each way); kernels without MFMA
+# compile to the same code either way.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -54,6 +54,7 @@ constexpr int kRows = 32;                 // queries per wave
 constexpr int kQTile = kWaves * kRows;    // queries per workgroup
 constexpr int kKeys = 32;                 // keys per tile
 constexpr int kTabCache = 2048;           // block-table entries kept in LDS
+constexpr float kSlack = 8.f;             // lazy-rescale slack, log2 units
 
 template <int D>
 struct Lds {
@@ -267,9 +268,15 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
 #pragma unroll
     for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[i]);
     tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32)) * p.scale_log2;
-    const float m_new = fmaxf(m_run, tile_max);
+    // Lazy rescaling: the reference m_run moves only when this tile's max
+    // exceeds it by more than kSlack (log2 units); otherwise the weights of
+    // the tile are at most 2^kSlack, well inside fp16 and fp32.  Numerator
+    // and denominator share the reference, so the result is the same
+    // softmax; the output is rescaled only when some query's reference moves.
+    const bool bump = tile_max > m_run + kSlack;
+    const float m_new = bump ? tile_max : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
     half8 pb[2];
 #pragma unroll
@@ -285,7 +292,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     // O^T += V^T P^T.  k-step jj covers keys 16jj .. 16jj+15 in the order
     // the score registers hold them: slots 0..3 -> keys 16jj + 4g + e,
     // slots 4..7 -> keys 16jj + 8 + 4g + (e - 4).
-    if (__ballot(alpha != 1.f)) {   // the running max moved for some query
+    if (__ballot(bump)) {   // some query's reference moved
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
     }
