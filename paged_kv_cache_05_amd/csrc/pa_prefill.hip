@@ -11,7 +11,8 @@
 // with the context cut at the query's own position).
 //
 // One workgroup = one (head, sequence, tile of 128 queries); 4 waves of 32
-// queries each.  Per 32-key tile, on v_mfma_f32_32x32x16_f16:
+// queries each.  The waves share each staged K/V tile; a wave skips the
+// products of tiles past its last query and, holding no query, all of them.  Per 32-key tile, on v_mfma_f32_32x32x16_f16:
 //   * S^T = K Q^T: key rows are the A operand, the wave's 32 query rows the
 //     B operand (kept in registers for the whole loop).  The contraction
 //     over head_dim runs in a permuted order both operands share (lane
@@ -203,6 +204,11 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   const int last = min(m, (qt + 1) * kQTile) - 1;
   const int kv_end = bad_seq ? 0 : n - m + last + 1; // keys the workgroup needs
   const int wave_pos0 = n - m + qt * kQTile + w * kRows;   // the wave's first query position
+  // The wave's products are skipped when it holds no query of the chunk,
+  // and for key tiles past its last query (it still stages tiles and meets
+  // every barrier).
+  const bool wave_active = qt * kQTile + w * kRows < m && !bad_seq;
+  const int wave_last = n - m + min(m, qt * kQTile + (w + 1) * kRows) - 1;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
   constexpr int kSteps = D / 16;
@@ -244,6 +250,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     const _Float16 *ks = lds + buf * (L::kK + L::kV);
     const _Float16 *vs = ks + L::kK;
 
+    if (wave_active && t0 <= wave_last) {
     // S^T = K Q^T.  A operand: key row c, head-dim half g.
     float16v s = {};
     {
@@ -307,6 +314,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[jj], acc_o[dt], 0, 0, 0);
       }
     }
+    }   // wave_active
 
     if (more) {
       _Float16 *nk = lds + (buf ^ 1) * (L::kK + L::kV);
@@ -353,7 +361,7 @@ __device__ inline void prefill_dispatch(const PrefillParams &p, int h, int b, in
 
 // grid (heads, query tiles, sequences); tiles in descending order.
 template <int D, int B>
-__global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) prefill_kernel(const PrefillParams p) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
   __shared__ int32_t tab[kTabCache];
   prefill_dispatch<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y, lds,
@@ -362,7 +370,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(const PrefillParams p
 
 // grid (heads, items): items = sequence << 16 | query tile, heaviest first.
 template <int D, int B>
-__global__ void __launch_bounds__(kThreads) prefill_listed_kernel(const PrefillParams p,
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) prefill_listed_kernel(const PrefillParams p,
                                                                   const WorkList items) {
   __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
   __shared__ int32_t tab[kTabCache];

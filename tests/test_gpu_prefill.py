@@ -93,11 +93,13 @@ def test_prefill_listed_launch(pa, oracle_lib, device, name):
 
 
 def test_prefill_edges(pa, oracle_lib, device):
-    """Sequences with no queries beside one-token and tile-boundary chunks
-    (127, 128, 129 queries); rows of empty chunks are never written."""
+    """Sequences with no queries beside one-token chunks and chunks around
+    the 32-query wave and 256-query workgroup boundaries; rows of empty
+    chunks are never written."""
     announce("prefill edges")
     wl = W.prefill_small(seed=11, head_dim=128,
-                         groups=((0, [127]), (5, [0]), (0, [128]), (200, [0, 129]), (0, [1])))
+                         groups=((0, [127]), (5, [0]), (0, [128]), (200, [0, 129]), (0, [1]),
+                                 (0, [255]), (3, [256]), (0, [257]), (40, [33])))
     ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
                              wl.query_start, wl.scale)
     check(run_gpu(pa, wl, device), ref, "edges")
