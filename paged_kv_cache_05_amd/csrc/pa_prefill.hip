@@ -124,6 +124,10 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
     }
   }
   bool all = true;
+  // Element offset of a row: phys * (H B D) + (h B + t % B) D + d0, one
+  // 64-bit multiply-add; keys not read point at the pool's first row.
+  const uint32_t block_elems = (uint32_t)p.num_heads * B * D;
+  const uint32_t head_elems = (uint32_t)h * B * D;
 #pragma unroll
   for (int u = 0; u < NK; ++u) {
     const bool in = kt[u] < end;
@@ -131,8 +135,9 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
     r.kok[u] = ok;
     r.kbad[u] = in && !ok;
     all = all && ok;
-    const int64_t row = ok ? ((int64_t)kphys[u] * p.num_heads + h) * B + kt[u] % B : 0;
-    r.k[u] = load_half8(kh + row * D + kd[u]);
+    const uint32_t phys = ok ? (uint32_t)kphys[u] : 0u;
+    const uint32_t within = ok ? head_elems + (uint32_t)(kt[u] % B) * D : 0u;
+    r.k[u] = load_half8(kh + ((uint64_t)phys * block_elems + within + kd[u]));
   }
 #pragma unroll
   for (int u = 0; u < NV; ++u)
@@ -141,8 +146,9 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
       const bool ok = vt[u][s] < end && vphys[u][s] >= 0 && vphys[u][s] < p.num_blocks;
       r.vok[u][s] = ok;
       all = all && ok;
-      const int64_t row = ok ? ((int64_t)vphys[u][s] * p.num_heads + h) * B + vt[u][s] % B : 0;
-      r.v[u][s] = load_half8(vh + row * D + vd[u]);
+      const uint32_t phys = ok ? (uint32_t)vphys[u][s] : 0u;
+      const uint32_t within = ok ? head_elems + (uint32_t)(vt[u][s] % B) * D : 0u;
+      r.v[u][s] = load_half8(vh + ((uint64_t)phys * block_elems + within + vd[u]));
     }
   r.all_ok = __ballot(!all) == 0;   // uniform per wave
 }
