@@ -12,8 +12,10 @@ of a model shares them) so that repeats are not served from the 256 MiB
 Infinity Cache.
 
 Prints one JSON line.  Timing: HIP events on the stream the kernels run on
-(torch's current stream), around the whole timed region and around every
-pa_decode call (one kernel launch each), after W untimed warm-up steps.
+(torch's current stream) around the timed region of exactly K steps, after
+W untimed warm-up steps; then a second pass of K steps with events around
+every decode launch (its average duration is the roofline's), and the same
+steps replayed from a captured HIP graph (reported beside, not as value).
 
 Also times the CPU oracle on the host (the full batch of layer 0, all host
 threads) as a reported baseline, and checks sampled GPU rows against it.
@@ -424,6 +426,8 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="layer pools to rotate over")
     ap.add_argument("--partition", type=int, default=0, help="pa_decode partition_size (0: default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra HIP-graph replay measurement")
     ap.add_argument("--split-step", action="store_true",
                     help="pa_write_kv then pa_decode (two launches) instead of the fused "
                          "pa_decode_append")
@@ -504,18 +508,46 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    # The timed region: exactly K steps, events only at its two ends.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(K):
-        step(i, evs[i])
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_per_step = total_ms / K
+
+    # A second pass of K steps with HIP events around every decode launch,
+    # for the kernel's average launch duration (the roofline); its events
+    # are kept out of the timed region above.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    # The same steps replayed from a HIP graph (one captured step per layer
+    # pool), as a serving loop that captures its launches would run them.
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // L)
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(reps):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / (reps * L)
+        del g
 
     decode_bytes = wl.algorithmic_bytes()
     # the step's necessary traffic: every context token's K and V once (the
@@ -584,6 +616,8 @@ def main():
         "decode_bytes_per_call": decode_bytes,
         "timed_call_bytes": call_bytes,
         "decode_ms_mean": round(dec_mean, 5),
+        "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "graph_replay_GBps": None if graph_ms is None else round(step_bytes / (graph_ms * 1e-3) / 1e9, 1),
         "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_ms, [10, 50, 90])],
         "roofline": {
             "bound": "hbm",
