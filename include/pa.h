@@ -249,9 +249,10 @@ int pa_decode_append(void *out, const void *q, const void *new_key, const void *
  *
  * host_query_start (optional, host memory, num_seqs + 1 entries) is a host
  * copy of query_start: with it the library launches only the query tiles
- * that exist, heaviest first (the tiles whose queries see the most keys),
- * when there are at most 960 of them; host_context_lens (optional, host
- * memory) then refines that order.  Without them, or with more tiles, the
+ * that exist, when there are at most 960 of them, grouped by sequence
+ * (sequences in descending order of their heaviest tile, each sequence's
+ * tiles heaviest first; a tile's weight is the keys its last query sees);
+ * host_context_lens (optional, host memory) then refines that order.  Without them, or with more tiles, the
  * grid covers every (head, tile < max_query_len / 128, sequence) and empty
  * tiles exit at once.  A sequence's device query count must not exceed its
  * host one.  Results do not depend on the launch form.

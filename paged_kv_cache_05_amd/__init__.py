@@ -340,7 +340,7 @@ def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, 
     context_lens[b]-token context (int32 device tensors; query_start [N+1]).
     max_context_len and max_query_len are host-side bounds; host copies of
     query_start (and context_lens) let the library launch only the tiles
-    that exist, heaviest first."""
+    that exist, grouped by sequence, heaviest first."""
     import numpy as np
     import torch
     NB, H, B, D = k_pool.shape

@@ -179,8 +179,8 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 extern "C" {
 
 // Work list of the prefill: every (sequence, query tile) that the grid
-// would cover, heaviest first (keys the tile's last query sees, descending;
-// ties in natural order).  False if it does not fit a WorkList.
+// would cover, grouped by sequence (see the order below; a tile's weight is
+// the keys its last query sees).  False if it does not fit a WorkList.
 bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max_context_len,
                   int max_query_len, pa::WorkList *items) {
   const int tile = pa::prefill_query_tile();
@@ -201,8 +201,18 @@ bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max
                       (int64_t)n - m + std::min(m, (t + 1) * tile)});
     }
   }
-  std::stable_sort(list.begin(), list.end(),
-                   [](const Item &a, const Item &b) { return a.work > b.work; });
+  // Sequence-major: sequences by their heaviest tile, descending, and each
+  // sequence's tiles heaviest first.  The tiles of one sequence then run
+  // together and share the K/V rows they stream in the L2 (a head's
+  // workgroups all land on one XCD: the grid's fastest index is the head).
+  std::vector<int64_t> seq_work(num_seqs > 0 ? num_seqs : 1, 0);
+  for (const Item &it : list)
+    seq_work[it.code >> 16] = std::max(seq_work[it.code >> 16], it.work);
+  std::stable_sort(list.begin(), list.end(), [&](const Item &a, const Item &b) {
+    const int sa = (int)(a.code >> 16), sb = (int)(b.code >> 16);
+    if (sa != sb) return seq_work[sa] != seq_work[sb] ? seq_work[sa] > seq_work[sb] : sa < sb;
+    return a.work > b.work;
+  });
   items->count = (int)list.size();
   for (size_t i = 0; i < list.size(); ++i) items->item[i] = list[i].code;
   return true;

@@ -24,9 +24,14 @@
 //   * O^T += V^T P^T: P^T is the B operand straight from the score
 //     registers (converted to fp16, no shuffle); the key order this implies
 //     is matched by the A operand, V^T, read from LDS.
-// The workgroup's block-table entries are copied to LDS once, so the address
-// of every key row is one LDS read away.  K and V tiles go through LDS,
-// double-buffered: the next tile's global
+// A tile whose keys all precede the workgroup's last query and whose table
+// entries all lie in the pool (every tile but the last, normally) is
+// fetched from uniform row bases: its one to four table entries are scalar
+// loads, and each thread adds an offset fixed for the whole loop.  Other
+// tiles take the checked fetch, which reads each key's table entry (from an
+// LDS copy of the workgroup's entries when it fits) and stages keys past
+// the last query as zeros and rows of bad entries as NaN.  K and V tiles go
+// through LDS, double-buffered: the next tile's global
 // loads are in flight while the current tile's products run, and one
 // barrier per tile separates the two buffers.  K is stored row-major with a
 // 68-dword row (16-byte reads by 16 lanes hit 64 distinct banks); V is
@@ -34,7 +39,9 @@
 // of 18 dwords, which keeps both the pair writes and the 8-byte operand
 // reads free of bank conflicts.
 // Accumulation and the softmax are fp32; P is rounded to fp16 for the
-// second product.
+// second product, and the softmax denominator sums those rounded weights
+// (v_dot2 against ones, fp32 accumulation), so numerator and denominator
+// use the same P.
 #include <math.h>
 
 #include "pa_kernels.h"
@@ -70,6 +77,28 @@ struct Lds {
   static constexpr int kKChunks = (kKUnits + kThreads - 1) / kThreads;
   static constexpr int kVPairs = (kVUnits + kThreads - 1) / kThreads;
 };
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Lanes l and l ^ 32 combined.  v_permlane32_swap trades the upper half of
+// its first operand with the lower half of its second; applied to two
+// copies of x it leaves x[l] and x[l ^ 32] in every lane, one in each
+// register.  Written as inline assembly because this compiler's builtin for
+// the instruction hands back the first register twice.  The s_nop gives the
+// two wait states a permlane swap needs after a VALU write of its operands.
+__device__ inline void swap_halves(unsigned &a, unsigned &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline float half_max(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  swap_halves(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ inline float half_sum(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  swap_halves(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
 
 __device__ inline half8 load_half8(const _Float16 *p) {
   return *reinterpret_cast<const half8 *>(p);
@@ -151,6 +180,97 @@ __device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
       r.v[u][s] = load_half8(vh + ((uint64_t)phys * block_elems + within + vd[u]));
     }
   r.all_ok = __ballot(!all) == 0;   // uniform per wave
+}
+
+// Fast fetch, for a tile whose 32 keys all precede `end` and whose table
+// entries all lie inside the pool (the common case; the caller checks both
+// on uniform values).  The tile covers kTB consecutive table entries (one
+// entry for B >= 32); their row bases are uniform, so every load is a
+// scalar base plus a per-thread offset that does not change over the loop.
+template <int D, int B>
+struct FastFetch {
+  static constexpr int kTB = B >= kKeys ? 1 : kKeys / B;   // table entries per tile
+  static constexpr int kKPerRound = kThreads / (D / 8);     // keys one K chunk round covers
+  // K chunk round u covers keys kk0 + u * kKPerRound; with kKPerRound <= B
+  // its table entry is the same for every thread.
+  static constexpr bool kKUniform = kKPerRound <= B;
+  // Per thread, fixed over the loop: byte offsets inside a block (head,
+  // row, head-dim chunk) of the first K chunk and of the first key of the V
+  // pair (the second key is the next row), and their table entries.
+  uint32_t koff, voff;
+  int klb, vlb;
+};
+
+template <int D, int B>
+__device__ inline FastFetch<D, B> fast_fetch_setup(int h) {
+  FastFetch<D, B> f;
+  const uint32_t head_bytes = (uint32_t)h * B * D * 2;
+  const int kk = threadIdx.x / (D / 8);                       // < kKPerRound
+  f.klb = B >= kKeys ? 0 : kk / B;
+  f.koff = head_bytes + (uint32_t)((kk % B) * D + (threadIdx.x % (D / 8)) * 8) * 2;
+  const int unit = threadIdx.x;                               // V units past kVUnits load a
+  const int d0 = ((unit / (kKeys / 2)) * 8) % D;              // valid row and are not stored
+  const int k0 = 2 * (unit % (kKeys / 2));
+  f.vlb = B >= kKeys ? 0 : k0 / B;                            // k0 and k0 + 1 share an entry
+  f.voff = head_bytes + (uint32_t)((k0 % B) * D + d0) * 2;
+  return f;
+}
+
+// Reads the kTB table entries of the tile at t0 (uniform; t0 + kKeys <= end
+// guarantees they lie in the row) and says whether the fast fetch applies.
+template <int D, int B>
+__device__ inline bool fast_tile_ok(const PrefillParams &p,
+                                    const __attribute__((address_space(4))) int32_t *ctab,
+                                    int end, int t0, int32_t (&phys)[FastFetch<D, B>::kTB]) {
+  if (t0 + kKeys > end) return false;
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < FastFetch<D, B>::kTB; ++i) {
+    phys[i] = ctab[t0 / B + i];
+    ok = ok && phys[i] >= 0 && phys[i] < p.num_blocks;
+  }
+  return ok;
+}
+
+template <int D, int B>
+__device__ inline void fetch_tile_fast(const PrefillParams &p, const FastFetch<D, B> &f,
+                                       const int32_t (&phys)[FastFetch<D, B>::kTB], int t0,
+                                       TileLoads<D, B> &r) {
+  using F = FastFetch<D, B>;
+  constexpr int kTB = F::kTB;
+  const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
+  const uint64_t row0 = B > kKeys ? (uint64_t)(t0 % B) * D * 2 : 0;   // tile inside one block
+  uint64_t base[kTB];
+#pragma unroll
+  for (int i = 0; i < kTB; ++i) base[i] = (uint64_t)(uint32_t)phys[i] * block_bytes + row0;
+  const char *kp = static_cast<const char *>(p.k_pool);
+  const char *vp = static_cast<const char *>(p.v_pool);
+#pragma unroll
+  for (int u = 0; u < Lds<D>::kKChunks; ++u) {
+    uint64_t b;
+    if constexpr (F::kKUniform) {
+      // entry (u R) / B, row offset (u R) % B, both uniform
+      b = base[(u * F::kKPerRound) / B % kTB] + (uint64_t)((u * F::kKPerRound) % B) * D * 2;
+    } else {
+      // rows repeat every round; the entry moves by R / B per round
+      const int lb = f.klb + u * (F::kKPerRound / B);
+      b = base[0];
+#pragma unroll
+      for (int i = 1; i < kTB; ++i) b = lb == i ? base[i] : b;
+    }
+    r.k[u] = *reinterpret_cast<const half8 *>(kp + b + f.koff);
+  }
+#pragma unroll
+  for (int u = 0; u < Lds<D>::kVPairs; ++u) {
+    uint64_t b = base[0];
+#pragma unroll
+    for (int i = 1; i < kTB; ++i) b = f.vlb == i ? base[i] : b;
+    b += (uint64_t)u * (kThreads / (kKeys / 2)) * 8 * 2;   // next head-dim chunks
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      r.v[u][s] = *reinterpret_cast<const half8 *>(vp + b + f.voff + s * D * 2);
+  }
+  r.all_ok = true;
 }
 
 // Registers -> LDS buffers (K row-major, V transposed as key pairs).
@@ -242,9 +362,21 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const FastFetch<D, B> ff = fast_fetch_setup<D, B>(h);
+  const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
+  // One tile of K/V rows into registers: the fast fetch when the tile lies
+  // before kv_end with every table entry in the pool, else the checked one.
+  auto fetch = [&](int t, TileLoads<D, B> &r) {
+    int32_t phys[FastFetch<D, B>::kTB];
+    if (fast_tile_ok<D, B>(p, ctab, kv_end, t, phys))
+      fetch_tile_fast<D, B>(p, ff, phys, t, r);
+    else
+      fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, t, r);
+  };
+
   TileLoads<D, B> next;
   if (kv_end > 0) {
-    fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, 0, next);
+    fetch(0, next);
     store_tile<D, B>(next, lds, lds + L::kK);
   }
   __syncthreads();
@@ -252,7 +384,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   int buf = 0;
   for (int t0 = 0; t0 < kv_end; t0 += kKeys) {
     const bool more = t0 + kKeys < kv_end;
-    if (more) fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, t0 + kKeys, next);
+    if (more) fetch(t0 + kKeys, next);
     const _Float16 *ks = lds + buf * (L::kK + L::kV);
     const _Float16 *vs = ks + L::kK;
 
@@ -280,7 +412,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     float tile_max = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[i]);
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32)) * p.scale_log2;
+    tile_max = half_max(tile_max) * p.scale_log2;
     // Lazy rescaling: the reference m_run moves only when this tile's max
     // exceeds it by more than kSlack (log2 units); otherwise the weights of
     // the tile are at most 2^kSlack, well inside fp16 and fp32.  Numerator
@@ -290,15 +422,18 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
     const float m_new = bump ? tile_max : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-    float psum = 0.f;
     half8 pb[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -m_use));
-      psum += e;
-      pb[i / 8][i % 8] = (_Float16)e;
-    }
-    psum += __shfl_xor(psum, 32);
+    for (int i = 0; i < 16; ++i)
+      pb[i / 8][i % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -m_use));
+    // The denominator sums the fp16 weights the second product uses.
+    float psum = 0.f;
+    const half2v one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      psum = __builtin_amdgcn_fdot2(half2v{pb[i / 4][2 * (i % 4)], pb[i / 4][2 * (i % 4) + 1]}, one,
+                                    psum, false);
+    psum = half_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
 
@@ -374,7 +509,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
                          (__attribute__((address_space(3))) int32_t *)tab);
 }
 
-// grid (heads, items): items = sequence << 16 | query tile, heaviest first.
+// grid (heads, items): items = sequence << 16 | query tile, in the order the
+// host planned.
 template <int D, int B>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) prefill_listed_kernel(const PrefillParams p,
                                                                   const WorkList items) {

@@ -62,6 +62,14 @@ CASES = {
                                              groups=((0, [130]), (33, [2, 97]), (64, [64]))),
     "small-b64-d128": lambda: W.prefill_small(seed=7, head_dim=128, block_size=64,
                                               groups=((0, [129]), (100, [1, 28]), (0, [2]))),
+    # every block size at both head sizes, so each way the tile fetch picks
+    # a row's table entry (one per tile, one per thread, inside one block)
+    # meets the oracle
+    "small-b8-d64": lambda: W.prefill_small(seed=12, block_size=8),
+    "small-b64-d64": lambda: W.prefill_small(seed=13, block_size=64,
+                                             groups=((0, [150]), (70, [3, 40]))),
+    "small-b32-d128": lambda: W.prefill_small(seed=14, head_dim=128, block_size=32,
+                                              groups=((0, [97]), (40, [70]), (64, [1, 9]))),
     "mix": lambda: W.prefill_mix(seed=8, num_heads=4, num_seqs=6, hi=700),
     "shared": lambda: W.prefill_shared(seed=9, num_heads=3, groups=2, members=4,
                                        prefix=(100, 400), suffix=(1, 200)),
@@ -80,7 +88,7 @@ def test_prefill_matches_oracle(pa, oracle_lib, device, name):
 @pytest.mark.parametrize("name", ["mix", "shared", "small-b8-d128", "small-b64-d128"])
 def test_prefill_listed_launch(pa, oracle_lib, device, name):
     """With host copies of query_start and context_lens the library launches
-    the existing tiles heaviest first: same oracle parity, and bit for bit
+    the existing tiles grouped by sequence: same oracle parity, and bit for bit
     the grid launch's output."""
     announce(f"prefill listed launch {name}")
     wl = CASES[name]()
