@@ -336,21 +336,6 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   const bool wave_active = qt * kQTile + w * kRows < m && !bad_seq;
   const int wave_last = n - m + min(m, qt * kQTile + (w + 1) * kRows) - 1;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-#ifndef PA_PF_PRIO
-#define PA_PF_PRIO 0
-#endif
-#if PA_PF_PRIO == 1
-  {
-    const int q4 = 4 * kv_end / max(p.max_context_len, 1);
-    if (q4 >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (q4 == 2) __builtin_amdgcn_s_setprio(2);
-    else if (q4 == 1) __builtin_amdgcn_s_setprio(1);
-  }
-#elif PA_PF_PRIO == 2
-  if (2 * kv_end >= p.max_context_len) __builtin_amdgcn_s_setprio(3);
-#elif PA_PF_PRIO == 3
-  if (4 * kv_end >= 3 * p.max_context_len) __builtin_amdgcn_s_setprio(3);
-#endif
 
   constexpr int kSteps = D / 16;
   half8 qb[kSteps];
