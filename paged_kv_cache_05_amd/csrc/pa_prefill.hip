@@ -11,38 +11,39 @@
 // with the context cut at the query's own position).
 //
 // One workgroup = one (head, sequence, tile of 128 queries); 4 waves of 32
-// queries each.  The waves share each staged K/V tile; a wave skips the
-// products of tiles past its last query and, holding no query, all of them.  Per 32-key tile, on v_mfma_f32_32x32x16_f16:
-//   * S^T = K Q^T: key rows are the A operand, the wave's 32 query rows the
-//     B operand (kept in registers for the whole loop).  The contraction
-//     over head_dim runs in a permuted order both operands share (lane
-//     group g takes the half [g*D/2, (g+1)*D/2)), so each lane reads one
-//     contiguous half row.
+// queries each; keys in tiles of kKeys.  Per tile, on
+// v_mfma_f32_32x32x16_f16:
+//   * S^T = K Q^T, one 32-key block at a time: key rows are the A operand,
+//     the wave's 32 query rows the B operand (kept in registers for the
+//     whole loop).  The contraction over head_dim runs in a permuted order
+//     both operands share (lane group g takes the half [g*D/2, (g+1)*D/2)).
 //   * In the accumulator layout every lane holds 16 scores of one query
-//     (its column): the online softmax needs one exchange (lanes l, l ^ 32)
-//     per tile and rescaling the output is a per-lane multiply.
+//     per key block: the online softmax exchanges lanes l and l ^ 32 twice
+//     per tile, and rescaling the output is a per-lane multiply.
 //   * O^T += V^T P^T: P^T is the B operand straight from the score
-//     registers (converted to fp16, no shuffle); the key order this implies
-//     is matched by the A operand, V^T, read from LDS.
-// A tile whose keys all precede the workgroup's last query and whose table
-// entries all lie in the pool (every tile but the last, normally) is
-// fetched from uniform row bases: its one to four table entries are scalar
-// loads, and each thread adds an offset fixed for the whole loop.  Other
-// tiles take the checked fetch, which reads each key's table entry (from an
-// LDS copy of the workgroup's entries when it fits) and stages keys past
-// the last query as zeros and rows of bad entries as NaN.  K and V tiles go
-// through LDS, double-buffered: the next tile's global
-// loads are in flight while the current tile's products run, and one
-// barrier per tile separates the two buffers.  K is stored row-major with a
-// 68-dword row (16-byte reads by 16 lanes hit 64 distinct banks); V is
-// stored transposed, written as packed key pairs (32-bit stores) into rows
-// of 18 dwords, which keeps both the pair writes and the 8-byte operand
-// reads free of bank conflicts.
+//     registers (converted to fp16, no shuffle); V^T, the A operand, comes
+//     from the row-major V tile by transposing LDS reads
+//     (ds_read_b64_tr_b16), in the key order the score registers imply.
+// Staging: K and V tiles are double-buffered in LDS, row-major, each
+// 16-byte chunk at a row-dependent XOR position, which keeps the K reads
+// and the transposing V reads free of bank conflicts.  Each wave stages a
+// quarter of the tile's rows.  When its rows all precede the workgroup's
+// last query and their table entries lie in the pool (every tile but the
+// last, normally), it loads them straight from the pools into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane into consecutive LDS chunks;
+// the swizzle is applied by the choice of each lane's source chunk), from a
+// scalar row base plus a per-lane offset fixed for the whole loop.
+// Otherwise it takes a checked, synchronous fetch through registers that
+// stages keys past the last query as zeros and rows of entries outside the
+// pool as NaN (K) / zero (V).  The next tile's loads are in flight while
+// the current tile's products run; one barrier per tile.
 // Accumulation and the softmax are fp32; P is rounded to fp16 for the
 // second product, and the softmax denominator sums those rounded weights
 // (v_dot2 against ones, fp32 accumulation), so numerator and denominator
 // use the same P.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_kernels.h"
 #include "pa_prefill.h"
@@ -52,33 +53,45 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half16 __attribute__((ext_vector_type(16)));
-typedef unsigned uint8v __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) half8 lds_half8;
+typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;                 // queries per wave
 constexpr int kQTile = kWaves * kRows;    // queries per workgroup
 constexpr int kKeys = 32;                 // keys per tile
-constexpr int kTabCache = 2048;           // block-table entries kept in LDS
+constexpr int kKeyBlocks = kKeys / 32;    // 32-key blocks per tile
 constexpr float kSlack = 8.f;             // lazy-rescale slack, log2 units
 
 template <int D>
-struct Lds {
-  static constexpr int kRowK = D + 8;             // halves per K row (68 dwords at D = 128)
-  static constexpr int kRowV = kKeys + 4;         // halves per V^T row (18 dwords)
-  static constexpr int kK = kKeys * kRowK;        // halves per K buffer
-  static constexpr int kV = D * kRowV;            // halves per V^T buffer
-  // one tile: K chunks (16 bytes of one key row) and V units (8 head-dim
-  // values of a key pair); per thread, rounded up (the last round guarded)
-  static constexpr int kKUnits = kKeys * (D / 8);                // 512 at D = 128
-  static constexpr int kVUnits = (kKeys / 2) * (D / 8);          // 256 at D = 128
-  static constexpr int kKChunks = (kKUnits + kThreads - 1) / kThreads;
-  static constexpr int kVPairs = (kVUnits + kThreads - 1) / kThreads;
+struct Geo {
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTensorBytes = kKeys * kRowBytes;  // K or V of one tile
+  static constexpr int kStageBytes = 2 * kTensorBytes;
+  static constexpr int kWaveRows = kKeys / kWaves;        // rows each wave stages
+  static constexpr int kLoadRows = 64 / kChunks;          // rows one wave-wide load covers
+  static constexpr int kLoads = kWaveRows / kLoadRows;    // loads per wave per tensor
+  static_assert(kLoads >= 1 && kWaveRows % kLoadRows == 0, "tile geometry");
 };
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+// Chunk c of tile row r sits at chunk position c ^ swz(r).  K: the 16 (D =
+// 128) or 8 rows that 16 lanes read at one chunk index spread over all 64
+// banks.  V: the 4 rows a half-wave's transposing read covers, 4
+// consecutive chunks each, land in 4 disjoint 16-bank ranges.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
 
 // Lanes l and l ^ 32 combined.  v_permlane32_swap trades the upper half of
 // its first operand with the lower half of its second; applied to two
@@ -104,223 +117,124 @@ __device__ inline half8 load_half8(const _Float16 *p) {
   return *reinterpret_cast<const half8 *>(p);
 }
 
-template <int D, int B>
-struct TileLoads {
-  half8 k[Lds<D>::kKChunks];
-  half8 v[Lds<D>::kVPairs][2];
-  bool kok[Lds<D>::kKChunks], kbad[Lds<D>::kKChunks];
-  bool vok[Lds<D>::kVPairs][2];
-  bool all_ok;   // every key this wave loads comes from the pool (uniform per wave)
-};
-
-// Global -> registers for keys t0 .. t0+31; keys at or past `end` (the
-// workgroup's last query position + 1) are not read and stage as zeros, and
-// a key whose table entry lies outside the pool stages as NaN (K) / zero
-// (V).  Straight-line code: every table entry is read first, then every
-// row load is issued (from the pool's first row where the key is not
-// read, so that no load is conditional), so the loads overlap each other
-// and the current tile's products.  The table entry comes from the
-// workgroup's LDS copy when the whole row fits there (kLdsTable), else from
-// global memory; the two are separate instantiations, since a pointer that
-// could be either becomes a flat load whose wait also drains every global
-// load in flight.
-template <int D, int B, bool kLdsTable>
-__device__ inline void fetch_tile(const PrefillParams &p, const int32_t *table,
-                                  const __attribute__((address_space(3))) int32_t *tab, int h,
-                                  int end, int t0, TileLoads<D, B> &r) {
-  const _Float16 *kh = static_cast<const _Float16 *>(p.k_pool);
-  const _Float16 *vh = static_cast<const _Float16 *>(p.v_pool);
-  constexpr int NK = Lds<D>::kKChunks, NV = Lds<D>::kVPairs;
-  int kt[NK], kd[NK], vt[NV][2], vd[NV];
-  int32_t kphys[NK], vphys[NV][2];
-#pragma unroll
-  for (int u = 0; u < NK; ++u) {
-    const int chunk = threadIdx.x + u * kThreads;   // d-chunk fastest: coalesced rows
-    kt[u] = chunk < Lds<D>::kKUnits ? t0 + chunk / (D / 8) : end;
-    kd[u] = (chunk % (D / 8)) * 8;
-    const int j = kt[u] < end ? kt[u] / B : 0;
-    kphys[u] = kLdsTable ? tab[j] : table[j];
-  }
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int unit = threadIdx.x + u * kThreads;    // key pair fastest
-    vd[u] = (unit / (kKeys / 2)) * 8;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      vt[u][s] = unit < Lds<D>::kVUnits ? t0 + 2 * (unit % (kKeys / 2)) + s : end;
-      const int j = vt[u][s] < end ? vt[u][s] / B : 0;
-      vphys[u][s] = kLdsTable ? tab[j] : table[j];
-    }
-  }
-  bool all = true;
-  // Element offset of a row: phys * (H B D) + (h B + t % B) D + d0, one
-  // 64-bit multiply-add; keys not read point at the pool's first row.
-  const uint32_t block_elems = (uint32_t)p.num_heads * B * D;
-  const uint32_t head_elems = (uint32_t)h * B * D;
-#pragma unroll
-  for (int u = 0; u < NK; ++u) {
-    const bool in = kt[u] < end;
-    const bool ok = in && kphys[u] >= 0 && kphys[u] < p.num_blocks;
-    r.kok[u] = ok;
-    r.kbad[u] = in && !ok;
-    all = all && ok;
-    const uint32_t phys = ok ? (uint32_t)kphys[u] : 0u;
-    const uint32_t within = ok ? head_elems + (uint32_t)(kt[u] % B) * D : 0u;
-    r.k[u] = load_half8(kh + ((uint64_t)phys * block_elems + within + kd[u]));
-  }
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bool ok = vt[u][s] < end && vphys[u][s] >= 0 && vphys[u][s] < p.num_blocks;
-      r.vok[u][s] = ok;
-      all = all && ok;
-      const uint32_t phys = ok ? (uint32_t)vphys[u][s] : 0u;
-      const uint32_t within = ok ? head_elems + (uint32_t)(vt[u][s] % B) * D : 0u;
-      r.v[u][s] = load_half8(vh + ((uint64_t)phys * block_elems + within + vd[u]));
-    }
-  r.all_ok = __ballot(!all) == 0;   // uniform per wave
-}
-
-// Fast fetch, for a tile whose 32 keys all precede `end` and whose table
-// entries all lie inside the pool (the common case; the caller checks both
-// on uniform values).  The tile covers kTB consecutive table entries (one
-// entry for B >= 32); their row bases are uniform, so every load is a
-// scalar base plus a per-thread offset that does not change over the loop.
-template <int D, int B>
-struct FastFetch {
-  static constexpr int kTB = B >= kKeys ? 1 : kKeys / B;   // table entries per tile
-  static constexpr int kKPerRound = kThreads / (D / 8);     // keys one K chunk round covers
-  // K chunk round u covers keys kk0 + u * kKPerRound; with kKPerRound <= B
-  // its table entry is the same for every thread.
-  static constexpr bool kKUniform = kKPerRound <= B;
-  // Per thread, fixed over the loop: byte offsets inside a block (head,
-  // row, head-dim chunk) of the first K chunk and of the first key of the V
-  // pair (the second key is the next row), and their table entries.
-  uint32_t koff, voff;
-  int klb, vlb;
+// Per-lane byte offsets, fixed for the whole loop.
+template <int D>
+struct Offsets {
+  uint32_t gk[Geo<D>::kLoads], gv[Geo<D>::kLoads];   // staging, inside a block
+  uint32_t rk[D / 16];                               // K operand, per head-dim step
+  uint32_t rv[D / 32];                               // V^T operand, per 32 head dims
 };
 
 template <int D, int B>
-__device__ inline FastFetch<D, B> fast_fetch_setup(int h) {
-  FastFetch<D, B> f;
+__device__ inline Offsets<D> make_offsets(int h, int w, int lane) {
+  using G = Geo<D>;
+  Offsets<D> o;
   const uint32_t head_bytes = (uint32_t)h * B * D * 2;
-  const int kk = threadIdx.x / (D / 8);                       // < kKPerRound
-  f.klb = B >= kKeys ? 0 : kk / B;
-  f.koff = head_bytes + (uint32_t)((kk % B) * D + (threadIdx.x % (D / 8)) * 8) * 2;
-  const int unit = threadIdx.x;                               // V units past kVUnits load a
-  const int d0 = ((unit / (kKeys / 2)) * 8) % D;              // valid row and are not stored
-  const int k0 = 2 * (unit % (kKeys / 2));
-  f.vlb = B >= kKeys ? 0 : k0 / B;                            // k0 and k0 + 1 share an entry
-  f.voff = head_bytes + (uint32_t)((k0 % B) * D + d0) * 2;
-  return f;
-}
-
-// Reads the kTB table entries of the tile at t0 (uniform; t0 + kKeys <= end
-// guarantees they lie in the row) and says whether the fast fetch applies.
-template <int D, int B>
-__device__ inline bool fast_tile_ok(const PrefillParams &p,
-                                    const __attribute__((address_space(4))) int32_t *ctab,
-                                    int end, int t0, int32_t (&phys)[FastFetch<D, B>::kTB]) {
-  if (t0 + kKeys > end) return false;
-  bool ok = true;
+  const int pos = lane % G::kChunks, sub = lane / G::kChunks;
 #pragma unroll
-  for (int i = 0; i < FastFetch<D, B>::kTB; ++i) {
-    phys[i] = ctab[t0 / B + i];
-    ok = ok && phys[i] >= 0 && phys[i] < p.num_blocks;
+  for (int j = 0; j < G::kLoads; ++j) {
+    const int r = w * G::kWaveRows + j * G::kLoadRows + sub;   // tile row this lane fills
+    o.gk[j] = head_bytes + sub * G::kRowBytes + ((pos ^ swz_k<D>(r)) * 16);
+    o.gv[j] = head_bytes + sub * G::kRowBytes + ((pos ^ swz_v<D>(r)) * 16);
   }
-  return ok;
+  // K operand: lane (c, g) reads row c (plus 32 per key block; the swizzle
+  // repeats every 32 rows), chunk g D/16 + j at step j.
+  const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+    o.rk[j] = c * G::kRowBytes + (((g * (D / 16) + j) ^ swz_k<D>(c)) * 16);
+  // V^T operand by ds_read_b64_tr_b16: in each 16-lane group, result lane
+  // i gets element i % 4 of the 4 values read by lanes i / 4, 4 + i / 4,
+  // 8 + i / 4 and 12 + i / 4.  So source lane s of group grp reads key row
+  // 4 (grp / 2) + s / 4 (plus the k-step's base; +8 for the operand's
+  // upper four keys) at head dims 32 dt + 16 (grp % 2) + 4 (s % 4) .. +3,
+  // and result lane l holds head dim 32 dt + l % 32 of keys
+  // 16 kk + 8 (e / 4) + 4 (l / 32) + e % 4, the order of the score
+  // registers.  Adding 16 kk or 8 rows leaves the swizzle unchanged.
+  const int s = lane & 15, grp = lane >> 4;
+  const int row = 4 * (grp >> 1) + (s >> 2);
+  const int q = 2 * (grp & 1) + ((s & 3) >> 1);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+    o.rv[dt] = row * G::kRowBytes + (((dt * 4 + q) ^ swz_v<D>(row)) * 16) + (s & 1) * 8;
+  return o;
 }
 
+// Stages this wave's rows [w kWaveRows, (w+1) kWaveRows) of the tile at t0
+// into the stage buffer st (K, then V).
 template <int D, int B>
-__device__ inline void fetch_tile_fast(const PrefillParams &p, const FastFetch<D, B> &f,
-                                       const int32_t (&phys)[FastFetch<D, B>::kTB], int t0,
-                                       TileLoads<D, B> &r) {
-  using F = FastFetch<D, B>;
-  constexpr int kTB = F::kTB;
-  const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
-  const uint64_t row0 = B > kKeys ? (uint64_t)(t0 % B) * D * 2 : 0;   // tile inside one block
-  uint64_t base[kTB];
-#pragma unroll
-  for (int i = 0; i < kTB; ++i) base[i] = (uint64_t)(uint32_t)phys[i] * block_bytes + row0;
+__device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, int h, int w,
+                                  int lane, int kv_end, int t0, lds_char *st,
+                                  const Offsets<D> &o) {
+  using G = Geo<D>;
+  const int r0 = w * G::kWaveRows;
+  const int key0 = t0 + r0;
+  constexpr int kEnt = B >= G::kWaveRows ? 1 : G::kWaveRows / B;
   const char *kp = static_cast<const char *>(p.k_pool);
   const char *vp = static_cast<const char *>(p.v_pool);
+  const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
+  bool fast = key0 + G::kWaveRows <= kv_end;
+  int32_t phys[kEnt];
+  if (fast) {
+    // uniform entries by scalar loads; the rows all precede kv_end, so the
+    // entries lie inside the table row
+    const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
 #pragma unroll
-  for (int u = 0; u < Lds<D>::kKChunks; ++u) {
-    uint64_t b;
-    if constexpr (F::kKUniform) {
-      // entry (u R) / B, row offset (u R) % B, both uniform
-      b = base[(u * F::kKPerRound) / B % kTB] + (uint64_t)((u * F::kKPerRound) % B) * D * 2;
-    } else {
-      // rows repeat every round; the entry moves by R / B per round
-      const int lb = f.klb + u * (F::kKPerRound / B);
-      b = base[0];
-#pragma unroll
-      for (int i = 1; i < kTB; ++i) b = lb == i ? base[i] : b;
+    for (int e = 0; e < kEnt; ++e) {
+      phys[e] = ctab[key0 / B + e];
+      fast = fast && phys[e] >= 0 && phys[e] < p.num_blocks;
     }
-    r.k[u] = *reinterpret_cast<const half8 *>(kp + b + f.koff);
   }
+  if (fast) {
 #pragma unroll
-  for (int u = 0; u < Lds<D>::kVPairs; ++u) {
-    uint64_t b = base[0];
-#pragma unroll
-    for (int i = 1; i < kTB; ++i) b = f.vlb == i ? base[i] : b;
-    b += (uint64_t)u * (kThreads / (kKeys / 2)) * 8 * 2;   // next head-dim chunks
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      r.v[u][s] = *reinterpret_cast<const half8 *>(vp + b + f.voff + s * D * 2);
+    for (int j = 0; j < G::kLoads; ++j) {
+      // a load's rows share one table entry: it covers kLoadRows <= B
+      // aligned rows
+      const int rj = r0 + j * G::kLoadRows;
+      const int e = B >= G::kWaveRows ? 0 : (j * G::kLoadRows) / B;
+      const uint64_t base =
+          (uint64_t)(uint32_t)phys[e] * block_bytes + (uint64_t)((t0 + rj) % B) * G::kRowBytes;
+      __builtin_amdgcn_global_load_lds(kp + base + o.gk[j], st + rj * G::kRowBytes, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + base + o.gv[j],
+                                       st + G::kTensorBytes + rj * G::kRowBytes, 16, 0, 0);
+    }
+    return;
   }
-  r.all_ok = true;
+  // Checked fetch: per lane, the same row and chunk as the direct load.
+  const int pos = lane % G::kChunks, sub = lane / G::kChunks;
+  const uint64_t head_bytes = (uint64_t)h * B * D * 2;
+#pragma unroll
+  for (int j = 0; j < G::kLoads; ++j) {
+    const int rj = r0 + j * G::kLoadRows;
+    const int r = rj + sub;
+    const int key = t0 + r;
+    const bool in = key < kv_end;
+    const int32_t ph = in ? table[key / B] : 0;
+    const bool ok = in && ph >= 0 && ph < p.num_blocks;
+    const uint64_t row =
+        ok ? (uint64_t)(uint32_t)ph * block_bytes + head_bytes + (uint64_t)(key % B) * G::kRowBytes
+           : 0;
+    half8 kx = *reinterpret_cast<const half8 *>(kp + row + (pos ^ swz_k<D>(r)) * 16);
+    half8 vx = *reinterpret_cast<const half8 *>(vp + row + (pos ^ swz_v<D>(r)) * 16);
+    if (!ok) {
+      kx = in ? half8{} + (_Float16)NAN : half8{};   // NaN for every query that sees it
+      vx = half8{};
+    }
+    *reinterpret_cast<lds_half8 *>(st + rj * G::kRowBytes + lane * 16) = kx;
+    *reinterpret_cast<lds_half8 *>(st + G::kTensorBytes + rj * G::kRowBytes + lane * 16) = vx;
+  }
 }
 
-// Registers -> LDS buffers (K row-major, V transposed as key pairs).
 template <int D, int B>
-__device__ inline void store_tile(const TileLoads<D, B> &r, _Float16 *ks, _Float16 *vs) {
-#pragma unroll
-  for (int u = 0; u < Lds<D>::kKChunks; ++u) {
-    const int chunk = threadIdx.x + u * kThreads;
-    if (chunk < Lds<D>::kKUnits) {
-      const int key = chunk / (D / 8), d0 = (chunk % (D / 8)) * 8;
-      half8 v = r.k[u];
-      if (!r.all_ok) {
-        if (!r.kok[u]) v = half8{};
-        if (r.kbad[u]) v = half8{} + (_Float16)NAN;   // NaN for every query that sees it
-      }
-      *reinterpret_cast<half8 *>(ks + key * Lds<D>::kRowK + d0) = v;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < Lds<D>::kVPairs; ++u) {
-    const int unit = threadIdx.x + u * kThreads;
-    if (unit < Lds<D>::kVUnits) {
-      const int kp = unit % (kKeys / 2), d0 = (unit / (kKeys / 2)) * 8;
-      // word e = (key 2kp, key 2kp+1) at head-dim d0 + e
-      half8 v0 = r.v[u][0], v1 = r.v[u][1];
-      if (!r.all_ok) {
-        if (!r.vok[u][0]) v0 = half8{};
-        if (!r.vok[u][1]) v1 = half8{};
-      }
-      const half16 z = __builtin_shufflevector(v0, v1, 0, 8, 1, 9, 2, 10, 3, 11,
-                                               4, 12, 5, 13, 6, 14, 7, 15);
-      const uint8v words = __builtin_bit_cast(uint8v, z);
-      unsigned *col = reinterpret_cast<unsigned *>(vs + d0 * Lds<D>::kRowV + 2 * kp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) col[e * (Lds<D>::kRowV / 2)] = words[e];
-    }
-  }
-}
-
-template <int D, int B, bool kLdsTable>
-__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Float16 *lds,
-                             __attribute__((address_space(3))) int32_t *tab) {
-  using L = Lds<D>;
+__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds) {
+  using G = Geo<D>;
   const int q0 = p.query_start[b];
   const int m = p.query_start[b + 1] - q0;
   const int n = min(max(p.context_lens[b], 0), p.max_context_len);
   if (qt * kQTile >= m) return;
   const bool bad_seq = m < 0 || m > n || q0 < 0 || q0 + m > p.num_query_rows;
 
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 31;                 // this lane's query column / key row
   const int g = lane >> 5;                 // lane group
@@ -331,11 +245,12 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   const int kv_end = bad_seq ? 0 : n - m + last + 1; // keys the workgroup needs
   const int wave_pos0 = n - m + qt * kQTile + w * kRows;   // the wave's first query position
   // The wave's products are skipped when it holds no query of the chunk,
-  // and for key tiles past its last query (it still stages tiles and meets
-  // every barrier).
+  // and for key tiles past its last query (it still stages its rows and
+  // meets every barrier).
   const bool wave_active = qt * kQTile + w * kRows < m && !bad_seq;
   const int wave_last = n - m + min(m, qt * kQTile + (w + 1) * kRows) - 1;
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+  const Offsets<D> o = make_offsets<D, B>(h, w, lane);
 
   constexpr int kSteps = D / 16;
   half8 qb[kSteps];
@@ -351,118 +266,110 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // The table entries the workgroup needs, once, into LDS.
-  if (kLdsTable) {
-    const int nblk = (kv_end + B - 1) / B;      // at most kTabCache here
-    for (int j = threadIdx.x; j < nblk; j += kThreads) tab[j] = table[j];
-  }
-  // Drain the query and table loads here, once: memory counters retire in
-  // order, so a wait for the query fragments inside the loop would also
-  // wait for the next tile's loads issued just before it.
-  __builtin_amdgcn_s_waitcnt(0);
+  if (kv_end > 0) stage_rows<D, B>(p, table, h, w, lane, kv_end, 0, lds, o);
+  __builtin_amdgcn_s_waitcnt(0);   // query fragments and the first tile
   __syncthreads();
 
-  const FastFetch<D, B> ff = fast_fetch_setup<D, B>(h);
-  const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
-  // One tile of K/V rows into registers: the fast fetch when the tile lies
-  // before kv_end with every table entry in the pool, else the checked one.
-  auto fetch = [&](int t, TileLoads<D, B> &r) {
-    int32_t phys[FastFetch<D, B>::kTB];
-    if (fast_tile_ok<D, B>(p, ctab, kv_end, t, phys))
-      fetch_tile_fast<D, B>(p, ff, phys, t, r);
-    else
-      fetch_tile<D, B, kLdsTable>(p, table, tab, h, kv_end, t, r);
-  };
-
-  TileLoads<D, B> next;
-  if (kv_end > 0) {
-    fetch(0, next);
-    store_tile<D, B>(next, lds, lds + L::kK);
-  }
-  __syncthreads();
-
-  int buf = 0;
-  for (int t0 = 0; t0 < kv_end; t0 += kKeys) {
-    const bool more = t0 + kKeys < kv_end;
-    if (more) fetch(t0 + kKeys, next);
-    const _Float16 *ks = lds + buf * (L::kK + L::kV);
-    const _Float16 *vs = ks + L::kK;
-
+  // One tile: stage the next one into the other buffer, run the products on
+  // this one, then wait for this wave's loads and meet the others.  The two
+  // buffers alternate by template argument, so every LDS offset is an
+  // immediate.
+  auto step = [&](auto stage, int t0) {
+    constexpr int kS = decltype(stage)::value;
+    lds_char *cur = lds + kS * G::kStageBytes;
+    if (t0 + kKeys < kv_end)
+      stage_rows<D, B>(p, table, h, w, lane, kv_end, t0 + kKeys, lds + (kS ^ 1) * G::kStageBytes, o);
     if (wave_active && t0 <= wave_last) {
-    // S^T = K Q^T.  A operand: key row c, head-dim half g.
-    float16v s = {};
-    {
-      const _Float16 *krow = ks + c * L::kRowK + g * (D / 2);
+      const lds_char *ks = cur;
+      const lds_char *vs = cur + G::kTensorBytes;
+      // S^T = K Q^T per 32-key block.
+      float16v s[kKeyBlocks];
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(load_half8(krow + 8 * j), qb[j], s, 0, 0, 0);
-    }
+      for (int kb = 0; kb < kKeyBlocks; ++kb) {
+        s[kb] = float16v{};
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+          const half8 a = *reinterpret_cast<const lds_half8 *>(ks + o.rk[j] + kb * 32 * G::kRowBytes);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[j], s[kb], 0, 0, 0);
+        }
+      }
+      // Online softmax for this lane's query over the tile's visible keys.
+      // The maximum is taken on raw scores (the scale is positive) and the
+      // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
+      // Tiles wholly at or below every query of the wave skip the mask.
+      if (t0 + kKeys - 1 > wave_pos0) {
+#pragma unroll
+        for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t0 + 32 * kb + (i / 4) * 8 + g * 4 + (i % 4);
+            if (key > pos) s[kb][i] = -INFINITY;
+          }
+      }
+      float tile_max = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[kb][i]);
+      tile_max = half_max(tile_max) * p.scale_log2;
+      // Lazy rescaling: the reference m_run moves only when this tile's max
+      // exceeds it by more than kSlack (log2 units); otherwise the weights
+      // of the tile are at most 2^kSlack, well inside fp16 and fp32.
+      // Numerator and denominator share the reference, so the result is the
+      // same softmax; the output is rescaled only when some query's
+      // reference moves.
+      const bool bump = tile_max > m_run + kSlack;
+      const float m_new = bump ? tile_max : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      half8 pb[kKeyBlocks][2];
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pb[kb][i / 8][i % 8] =
+              (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -m_use));
+      // The denominator sums the fp16 weights the second product uses.
+      float psum = 0.f;
+      const half2v one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+      for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          psum = __builtin_amdgcn_fdot2(
+              half2v{pb[kb][i / 4][2 * (i % 4)], pb[kb][i / 4][2 * (i % 4) + 1]}, one, psum, false);
+      psum = half_sum(psum);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
 
-    // Online softmax for this lane's query over the tile's visible keys.
-    // The maximum is taken on raw scores (the scale is positive) and the
-    // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
-    // Tiles wholly at or below every query of the wave skip the mask.
-    if (t0 + kKeys - 1 > wave_pos0) {
+      if (__ballot(bump)) {   // some query's reference moved
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = t0 + (i / 4) * 8 + g * 4 + (i % 4);
-        if (key > pos) s[i] = -INFINITY;
+        for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
+      }
+      // O^T += V^T P^T.  k-step kk covers keys 16 kk .. 16 kk + 15 in the
+      // order the score registers hold them: slots 0..3 -> keys
+      // 16 kk + 4 g + e, slots 4..7 -> keys 16 kk + 8 + 4 g + (e - 4).
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int kk = 0; kk < kKeys / 16; ++kk) {
+          const lds_char *vrow = vs + o.rv[dt] + 16 * kk * G::kRowBytes;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)vrow);
+          const short4v hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(vrow + 8 * G::kRowBytes));
+          const half8 a = __builtin_bit_cast(
+              half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk / 2][kk % 2], acc_o[dt], 0, 0, 0);
+        }
       }
     }
-    float tile_max = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[i]);
-    tile_max = half_max(tile_max) * p.scale_log2;
-    // Lazy rescaling: the reference m_run moves only when this tile's max
-    // exceeds it by more than kSlack (log2 units); otherwise the weights of
-    // the tile are at most 2^kSlack, well inside fp16 and fp32.  Numerator
-    // and denominator share the reference, so the result is the same
-    // softmax; the output is rescaled only when some query's reference moves.
-    const bool bump = tile_max > m_run + kSlack;
-    const float m_new = bump ? tile_max : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-    half8 pb[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pb[i / 8][i % 8] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[i], p.scale_log2, -m_use));
-    // The denominator sums the fp16 weights the second product uses.
-    float psum = 0.f;
-    const half2v one = {(_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      psum = __builtin_amdgcn_fdot2(half2v{pb[i / 4][2 * (i % 4)], pb[i / 4][2 * (i % 4) + 1]}, one,
-                                    psum, false);
-    psum = half_sum(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // O^T += V^T P^T.  k-step jj covers keys 16jj .. 16jj+15 in the order
-    // the score registers hold them: slots 0..3 -> keys 16jj + 4g + e,
-    // slots 4..7 -> keys 16jj + 8 + 4g + (e - 4).
-    if (__ballot(bump)) {   // some query's reference moved
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const _Float16 *vrow = vs + (dt * 32 + c) * L::kRowV;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const half4 lo = *reinterpret_cast<const half4 *>(vrow + 16 * jj + 4 * g);
-        const half4 hi = *reinterpret_cast<const half4 *>(vrow + 16 * jj + 8 + 4 * g);
-        const half8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[jj], acc_o[dt], 0, 0, 0);
-      }
-    }
-    }   // wave_active
-
-    if (more) {
-      _Float16 *nk = lds + (buf ^ 1) * (L::kK + L::kV);
-      store_tile<D, B>(next, nk, nk + L::kK);
-    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int t0 = 0; t0 < kv_end; t0 += 2 * kKeys) {
+    step(std::integral_constant<int, 0>{}, t0);
+    if (t0 + kKeys >= kv_end) break;
+    step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
 
   if (r >= m || q0 + r >= p.num_query_rows || r < 0) return;
@@ -473,52 +380,38 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, _Floa
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      half4 o;
+      half4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (_Float16)(acc_o[dt][i4 * 4 + e] * inv);
-      *reinterpret_cast<half4 *>(orow + dt * 32 + i4 * 8 + g * 4) = o;
+      for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(acc_o[dt][i4 * 4 + e] * inv);
+      *reinterpret_cast<half4 *>(orow + dt * 32 + i4 * 8 + g * 4) = o4;
     }
 }
 
+// Waves per SIMD the register budget is set for (168 VGPRs).  Two stages of
+// 32-key tiles take 32 KB of LDS at D = 128.  64-key tiles (two waves per
+// SIMD) measured 5-12% slower.
 template <int D>
-constexpr int lds_halves() {
-  return 2 * (Lds<D>::kK + Lds<D>::kV);
-}
-
-// Dispatch on whether the workgroup's table row fits its LDS copy (uniform
-// per workgroup).
-template <int D, int B>
-__device__ inline void prefill_dispatch(const PrefillParams &p, int h, int b, int qt,
-                                        _Float16 *lds,
-                                        __attribute__((address_space(3))) int32_t *tab) {
-  const int m = p.query_start[b + 1] - p.query_start[b];
-  const int n = min(max(p.context_lens[b], 0), p.max_context_len);
-  const int last_key = n - m + min(m, (qt + 1) * kQTile);   // kv_end when the chunk is valid
-  if ((last_key + B - 1) / B <= kTabCache)
-    prefill_item<D, B, true>(p, h, b, qt, lds, tab);
-  else
-    prefill_item<D, B, false>(p, h, b, qt, lds, tab);
+constexpr int waves_per_eu() {
+  return 3;
 }
 
 // grid (heads, query tiles, sequences); tiles in descending order.
 template <int D, int B>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) prefill_kernel(const PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
-  __shared__ int32_t tab[kTabCache];
-  prefill_dispatch<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y, lds,
-                         (__attribute__((address_space(3))) int32_t *)tab);
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
+prefill_kernel(const PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
+  prefill_item<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y,
+                     (lds_char *)lds);
 }
 
 // grid (heads, items): items = sequence << 16 | query tile, in the order the
 // host planned.
 template <int D, int B>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) prefill_listed_kernel(const PrefillParams p,
-                                                                  const WorkList items) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds[lds_halves<D>()];
-  __shared__ int32_t tab[kTabCache];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
+prefill_listed_kernel(const PrefillParams p, const WorkList items) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
   const uint32_t it = items.item[blockIdx.y];
-  prefill_dispatch<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), lds,
-                         (__attribute__((address_space(3))) int32_t *)tab);
+  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds);
 }
 
 template <int D, int B>
