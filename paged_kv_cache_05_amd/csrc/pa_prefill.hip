@@ -372,7 +372,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
 
-  if (r >= m || q0 + r >= p.num_query_rows || r < 0) return;
+  if (r >= m || q0 + r >= p.num_query_rows || q0 + r < 0) return;   // rows in range only
   // Lane holds O^T[d][query c] for d = 32 dt + 8 (i/4) + 4 g + (i%4).
   const float inv = (bad_seq || !(l_run > 0.f)) ? NAN : 1.f / l_run;
   _Float16 *orow = static_cast<_Float16 *>(p.out) + ((int64_t)(q0 + r) * p.num_heads + h) * D;

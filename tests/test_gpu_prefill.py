@@ -144,6 +144,33 @@ def test_prefill_chunk_longer_than_context_is_nan(pa, oracle_lib, device):
     check(got[5:], ref[5:], "valid sequence")
 
 
+def test_prefill_rows_before_zero_are_not_written(pa, oracle_lib, device):
+    """A sequence whose device query_start is negative is invalid: its rows
+    that fall inside [0, num_query_rows) become NaN and the rows before row
+    0 are not written.  out is a view into a larger buffer, so a write
+    before it would land in the sentinel rows in front of it."""
+    announce("prefill negative query start")
+    import torch
+    wl = W.prefill_small(seed=15, groups=((0, [20]), (0, [9])))
+    qs = wl.query_start.copy()
+    qs[0] = -4                                   # sequence 0: rows -4 .. 19
+    T, H, D = wl.q.shape
+    pad = 8
+    big = torch.full((pad + T, H, D), 7.0, dtype=torch.float16, device=device)
+    out = big[pad:]
+    pa.pa_prefill(out, dev(wl.q, device), dev(wl.k_pool, device), dev(wl.v_pool, device),
+                  dev(wl.block_tables, device), dev(wl.context_lens, device), dev(qs, device),
+                  float(wl.scale), int(np.diff(qs).max()), int(np.diff(qs).max()))
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    assert (got[:pad] == 7.0).all(), "rows before row 0 were written"
+    n0 = int(wl.query_start[1])
+    assert np.isnan(got[pad:pad + n0]).all()
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(got[pad + n0:], ref[n0:], "other sequence")
+
+
 def sampled_rows(wl, per_seq, rng):
     """(sequence, first row, count) windows whose oracle values need only a
     truncated context: a query at position p sees tokens 0..p."""
