@@ -515,9 +515,8 @@ __global__ void __launch_bounds__(D) merge_listed_kernel(const DecodeParams p,
   merge_one<T, D>(p, blockIdx.x, (int)rows.item[blockIdx.y]);
 }
 
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 8
-#endif
+// Waves per workgroup: 8 (4 and 16 measured slower).
+constexpr int kDecodeWaves = 8;
 
 struct Lists {
   const WorkList *items, *merge_rows;
@@ -525,7 +524,7 @@ struct Lists {
 
 template <typename T, int D, int B>
 hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_t stream) {
-  constexpr int W = PA_DECODE_WAVES;  // waves per workgroup
+  constexpr int W = kDecodeWaves;
   if (l.items) {
     if (l.items->count > 0)
       decode_listed_kernel<T, D, B, W>
