@@ -100,7 +100,10 @@ def bench_prefill(args):
     (median 300, sigma 0.9, clipped [1, 2048]); (b) 4 groups x 8 requests
     sharing a cached prefix of 256..1024 tokens, each with its own 16..256
     query tokens.  Throughput = causal attention FLOPs (4 D per query, key
-    and head) / event-timed call."""
+    and head) / event-timed call.  Every call gets a 64-slot workspace (the
+    planner splits nothing in (a) or (b)); single requests (one 2048-token
+    prompt; 256 query tokens over a 4096-token cached prefix) are reported
+    beside, whole and split."""
     import torch
 
     import paged_kv_cache_05_amd as pa
@@ -110,15 +113,16 @@ def bench_prefill(args):
     K = max(1, min(args.steps, 50))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
     stream = torch.cuda.current_stream()
-    res = {}
-    for name, wl in (("mix", W.prefill_mix()), ("shared", W.prefill_shared())):
+    ws = pa.new_prefill_workspace(40, 128, slots=64, device=device)
+
+    def timed(wl, workspace):
         q, kp, vp = dev(wl.q), dev(wl.k_pool), dev(wl.v_pool)
         tables, ctx, qs = dev(wl.block_tables), dev(wl.context_lens), dev(wl.query_start)
         out = torch.empty_like(q)
         call = lambda: pa.pa_prefill(out, q, kp, vp, tables, ctx, qs, float(wl.scale),
                                      wl.max_context_len, wl.max_query_len,
                                      host_query_start=wl.query_start,
-                                     host_context_lens=wl.context_lens)
+                                     host_context_lens=wl.context_lens, workspace=workspace)
         for _ in range(max(args.warmup, 1)):
             call()
         torch.cuda.synchronize()
@@ -130,12 +134,28 @@ def bench_prefill(args):
             b.record(stream)
         torch.cuda.synchronize()
         ms = np.array([a.elapsed_time(b) for a, b in evs])
-        flops, nbytes = wl.algorithmic_flops(), wl.algorithmic_bytes()
         got = out.cpu().numpy()
         if not np.isfinite(got).all():
-            raise SystemExit(f"bench: non-finite prefill output ({name})")
-        res[name] = {"wl": wl, "ms": float(ms.mean()), "flops": flops, "bytes": nbytes,
-                     "out": got}
+            raise SystemExit(f"bench: non-finite prefill output ({wl.name})")
+        return float(ms.mean()), got
+
+    res = {}
+    for name, wl in (("mix", W.prefill_mix()), ("shared", W.prefill_shared())):
+        ms, got = timed(wl, ws)
+        res[name] = {"wl": wl, "ms": ms, "flops": wl.algorithmic_flops(),
+                     "bytes": wl.algorithmic_bytes(), "out": got}
+    # Single requests on an otherwise idle GPU, whole and with the key range
+    # of their heaviest query tiles split over the workspace.
+    single = {}
+    for name, groups in (("one_prompt_2048", ((0, [2048]),)),
+                         ("suffix_256_over_4096", ((4096, [256]),))):
+        wl = W.prefill_small(seed=51, num_heads=40, head_dim=128, block_size=16, groups=groups)
+        ms_whole, _ = timed(wl, None)
+        ms_split, _ = timed(wl, ws)
+        f = wl.algorithmic_flops() / 1e12
+        single[name] = {"ms_whole": round(ms_whole, 5), "ms_split": round(ms_split, 5),
+                        "TFLOPs_whole": round(f / (ms_whole * 1e-3), 2),
+                        "TFLOPs_split": round(f / (ms_split * 1e-3), 2)}
     mix = res["mix"]
     tflops = mix["flops"] / (mix["ms"] * 1e-3) / 1e12
 
@@ -183,6 +203,7 @@ def bench_prefill(args):
                           "query_tokens": int(sh["wl"].query_start[-1]),
                           "context_tokens": int(sh["wl"].context_lens.sum()),
                           "groups": sh["wl"].extra["groups"].__len__()},
+        "single_request": single,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

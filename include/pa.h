@@ -260,8 +260,18 @@ int pa_decode_append(void *out, const void *q, const void *new_key, const void *
  * A sequence whose m_b exceeds its (clamped) context, or whose rows fall
  * outside [0, num_query_rows), gets NaN rows (those in range); a table entry
  * outside the pool makes NaN every row that attends to its keys.  Rows past
- * max_query_len of a sequence are not written.  No workspace.  Asynchronous
- * on `stream`.
+ * max_query_len of a sequence are not written.  Asynchronous on `stream`.
+ *
+ * workspace (optional, device memory, 16-byte aligned, caller-owned;
+ * workspace_bytes long, see pa_prefill_workspace_bytes) lets the listed
+ * launch split the key range of its heaviest query tiles across several
+ * workgroups when those tiles alone would set the launch's length (a few
+ * long prompts, or a long cached prefix, on a mostly idle GPU).  The
+ * chunks write partial softmax states (max, sum, unnormalised output) to
+ * the workspace and a second kernel merges them.  Split results equal the
+ * unsplit ones up to fp32 rounding of the merge.  Without a workspace (NULL
+ * or fewer than two slots) nothing is split.  The workspace must not be in
+ * use by another call at the same time.
  */
 int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                const int32_t *block_tables, const int32_t *context_lens,
@@ -269,7 +279,15 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                int max_context_len, int max_query_len, float scale, int dtype,
                const int32_t *host_query_start, const int32_t *host_context_lens,
-               void *stream);
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of a pa_prefill workspace with room for `slots` partial results
+ * (one per key chunk of a split query tile, all heads):
+ * slots * num_heads * 128 * (head_dim * 4 + 8).  0 for invalid arguments
+ * (num_heads <= 0, head_dim not 64 or 128, slots <= 0).
+ */
+size_t pa_prefill_workspace_bytes(int num_heads, int head_dim, int slots);
 
 /*
  * Swapping: copy whole blocks between two pool pairs, typically the device

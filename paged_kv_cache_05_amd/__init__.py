@@ -46,7 +46,8 @@ def default_partition(max_context_len: int) -> int:
 
 # Every symbol include/pa.h and include/pa_manager.h declare.
 EXPORTS = ("pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
-           "pa_copy_blocks", "pa_swap_blocks", "pa_prefill", "pa_status_string", "pa_last_error",
+           "pa_copy_blocks", "pa_swap_blocks", "pa_prefill", "pa_prefill_workspace_bytes",
+           "pa_status_string", "pa_last_error",
            "pa_manager_create", "pa_manager_destroy", "pa_manager_add", "pa_manager_fork",
            "pa_manager_append", "pa_manager_free", "pa_manager_tables", "pa_manager_num_free",
            "pa_manager_num_sequences", "pa_manager_refcount", "pa_manager_length",
@@ -104,8 +105,10 @@ def library() -> ctypes.CDLL:
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                               i32, i32, f32, i32, vp, vp, vp]
+                               i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.pa_prefill.restype = i32
+    lib.pa_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.pa_prefill_workspace_bytes.restype = sz
     lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -183,6 +186,21 @@ def pa_decode_partition_size(num_seqs, num_heads, head_dim, max_context_len, par
     if n < 0:
         raise PAError(f"pa_decode_partition_size: {pa_status_string(n)} ({n})")
     return int(n)
+
+
+def pa_prefill_workspace_bytes(num_heads, head_dim, slots) -> int:
+    """Bytes of a pa_prefill workspace with `slots` partial-result slots."""
+    n = library().pa_prefill_workspace_bytes(int(num_heads), int(head_dim), int(slots))
+    if n == 0:
+        raise PAError("pa_prefill_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def new_prefill_workspace(num_heads, head_dim, slots=64, device="cuda"):
+    """A pa_prefill workspace of `slots` partial-result slots."""
+    import torch
+    return torch.empty(pa_prefill_workspace_bytes(num_heads, head_dim, slots), dtype=torch.uint8,
+                       device=device)
 
 
 def new_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size=0,
@@ -334,13 +352,16 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None):
 
 def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
                max_context_len, max_query_len, stream=None, host_query_start=None,
-               host_context_lens=None):
+               host_context_lens=None, workspace=None):
     """out[T][H][D] = causal paged prefill attention of q[T][H][D]: sequence
     b's rows query_start[b] .. query_start[b+1]-1 are the last tokens of its
     context_lens[b]-token context (int32 device tensors; query_start [N+1]).
     max_context_len and max_query_len are host-side bounds; host copies of
     query_start (and context_lens) let the library launch only the tiles
-    that exist, grouped by sequence, heaviest first."""
+    that exist, grouped by sequence, heaviest first.  workspace (optional,
+    a device uint8 tensor, see new_prefill_workspace) lets that launch split
+    the key range of its heaviest tiles when they alone would set its
+    length."""
     import numpy as np
     import torch
     NB, H, B, D = k_pool.shape
@@ -364,7 +385,9 @@ def pa_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, 
         _dev(query_start, "query_start", torch.int32), N, T, H, D, B, NB,
         block_tables.shape[1], int(max_context_len), int(max_query_len), float(scale),
         _dtype_code(q), None if hqs is None else hqs.ctypes.data,
-        None if hctx is None else hctx.ctypes.data, _stream(stream))
+        None if hctx is None else hctx.ctypes.data,
+        None if workspace is None else _dev(workspace, "workspace", torch.uint8),
+        0 if workspace is None else workspace.numel(), _stream(stream))
     _check(rc, "pa_prefill")
 
 

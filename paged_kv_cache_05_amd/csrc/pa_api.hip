@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "pa.h"
@@ -179,17 +180,20 @@ int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int hea
 extern "C" {
 
 // Work list of the prefill: every (sequence, query tile) that the grid
-// would cover, grouped by sequence (see the order below; a tile's weight is
-// the keys its last query sees).  False if it does not fit a WorkList.
+// would cover, with its weight (the keys its last query sees), grouped by
+// sequence (see the order below).  False if it has more than kMaxListed
+// entries.
+struct PrefillItem {
+  uint32_t code;   // sequence << 16 | query tile
+  int64_t work;
+};
+
 bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max_context_len,
-                  int max_query_len, pa::WorkList *items) {
+                  int max_query_len, std::vector<PrefillItem> *out) {
   const int tile = pa::prefill_query_tile();
   const int max_tiles = (max_query_len + tile - 1) / tile;
-  struct Item {
-    uint32_t code;
-    int64_t work;
-  };
-  std::vector<Item> list;
+  std::vector<PrefillItem> &list = *out;
+  list.clear();
   for (int b = 0; b < num_seqs; ++b) {
     const int m = hqs[b + 1] - hqs[b];
     if (m <= 0) continue;
@@ -206,16 +210,109 @@ bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max
   // together and share the K/V rows they stream in the L2 (a head's
   // workgroups all land on one XCD: the grid's fastest index is the head).
   std::vector<int64_t> seq_work(num_seqs > 0 ? num_seqs : 1, 0);
-  for (const Item &it : list)
+  for (const PrefillItem &it : list)
     seq_work[it.code >> 16] = std::max(seq_work[it.code >> 16], it.work);
-  std::stable_sort(list.begin(), list.end(), [&](const Item &a, const Item &b) {
+  std::stable_sort(list.begin(), list.end(), [&](const PrefillItem &a, const PrefillItem &b) {
     const int sa = (int)(a.code >> 16), sb = (int)(b.code >> 16);
     if (sa != sb) return seq_work[sa] != seq_work[sb] ? seq_work[sa] > seq_work[sb] : sa < sb;
     return a.work > b.work;
   });
-  items->count = (int)list.size();
-  for (size_t i = 0; i < list.size(); ++i) items->item[i] = list[i].code;
   return true;
+}
+
+// Prefill workgroups the current device holds at once (CUs times the
+// kernel's workgroups per CU), cached per device; 0 if unknown.
+int prefill_resident_groups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return 0;
+    v = cus * pa::prefill_groups_per_cu();
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Split plan.  When the launch leaves the GPU mostly idle (its tiles times
+// heads fall short of two workgroups per CU), the idle slots take extra key
+// chunks: the tile whose current chunk has the most key tiles gets one more
+// chunk (all heads), if it has at least 48 key tiles, its chunks stay at
+// least 16 key tiles long, it has at most kMaxChunks and workspace slots
+// last.  The chunks of a split tile run side by side and a merge pass
+// combines them.  A launch that already fills the GPU is never split.
+// False when no tile is split or the launch list would not fit: the plain
+// list is used.
+bool plan_prefill_split(const std::vector<PrefillItem> &list, int num_heads, int resident,
+                        size_t slots, pa::SplitList *split, pa::SplitList *merges) {
+  if (list.empty() || resident <= 0 || slots < 2) return false;
+  const int kt = pa::prefill_key_tile();
+  // Measured on 40 heads x 128 (single prompts of 1024..4096 tokens, one or
+  // a few; suffixes of 64..256 queries over 2048..8192 cached tokens):
+  // shorter tiles, shorter chunks or more than two workgroups per CU cost
+  // full prompts time (partial results are fp32 rows of 512 bytes per query
+  // and head, written and read back).
+  constexpr int64_t kMinSplitTiles = 48, kMinChunkTiles = 16;
+  int64_t free_groups = (int64_t)resident * 2 / pa::prefill_groups_per_cu() -
+                        (int64_t)list.size() * num_heads;
+  if (free_groups < num_heads) return false;
+  std::vector<int> chunks(list.size(), 1);
+  std::vector<int64_t> tiles(list.size());
+  for (size_t i = 0; i < list.size(); ++i) tiles[i] = (list[i].work + kt - 1) / kt;
+  // largest current chunk first (tiles / chunks, rounded up)
+  auto chunk_len = [&](size_t i) { return (tiles[i] + chunks[i] - 1) / chunks[i]; };
+  std::vector<size_t> heap(list.size());
+  for (size_t i = 0; i < heap.size(); ++i) heap[i] = i;
+  auto less = [&](size_t a, size_t b) { return chunk_len(a) < chunk_len(b); };
+  std::make_heap(heap.begin(), heap.end(), less);
+  size_t used = 0;
+  while (!heap.empty() && free_groups >= num_heads) {
+    std::pop_heap(heap.begin(), heap.end(), less);
+    const size_t i = heap.back();
+    heap.pop_back();
+    const int nc = chunks[i] + 1;
+    const size_t need = nc == 2 ? 2 : 1;   // slots this step takes
+    if (tiles[i] < kMinSplitTiles || nc > pa::kMaxChunks || tiles[i] / nc < kMinChunkTiles ||
+        used + need > slots)
+      continue;
+    chunks[i] = nc;
+    used += need;
+    free_groups -= num_heads;
+    heap.push_back(i);
+    std::push_heap(heap.begin(), heap.end(), less);
+  }
+  if (used == 0) return false;
+  size_t entries = 0;
+  for (int nc : chunks) entries += nc;
+  if (entries > (size_t)pa::kMaxSplitItems) return false;
+  split->count = 0;
+  merges->count = 0;
+  uint32_t slot = 0;
+  for (size_t i = 0; i < list.size(); ++i) {
+    const int nc = chunks[i];
+    for (int c = 0; c < nc; ++c) {
+      split->item[split->count] = list[i].code;
+      split->part[split->count] =   // each chunk its own slot: slot + c
+          nc > 1 ? ((slot + (uint32_t)c) << 8 | (uint32_t)c << 4 | (uint32_t)(nc - 1)) : 0u;
+      ++split->count;
+    }
+    if (nc > 1) {
+      merges->item[merges->count] = list[i].code;
+      merges->part[merges->count] = slot << 8 | (uint32_t)(nc - 1);
+      ++merges->count;
+      slot += (uint32_t)nc;
+    }
+  }
+  return true;
+}
+
+size_t pa_prefill_workspace_bytes(int num_heads, int head_dim, int slots) {
+  if (num_heads <= 0 || (head_dim != 64 && head_dim != 128) || slots <= 0) return 0;
+  return pa::prefill_slot_bytes(num_heads, head_dim) * (size_t)slots;
 }
 
 int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
@@ -224,7 +321,7 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
                int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
                int max_context_len, int max_query_len, float scale, int dtype,
                const int32_t *host_query_start, const int32_t *host_context_lens,
-               void *stream) {
+               void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
   if (dtype != PA_F16) return PA_ERR_UNSUPPORTED;
@@ -237,7 +334,7 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
     return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
-      ((uintptr_t)query_start & 3u))
+      ((uintptr_t)query_start & 3u) || (workspace && !aligned16(workspace)))
     return PA_ERR_SHAPE;
   const int64_t tiles = ((int64_t)max_query_len + pa::prefill_query_tile() - 1) /
                         pa::prefill_query_tile();
@@ -256,13 +353,32 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
   p.max_context_len = max_context_len;
   p.num_query_rows = num_query_rows;
   p.scale_log2 = scale * 1.44269504088896340736f;
-  pa::WorkList items;
+  std::vector<PrefillItem> list;
   const bool listed = host_query_start &&
                       plan_prefill(host_query_start, host_context_lens, num_seqs,
-                                   max_context_len, max_query_len, &items);
+                                   max_context_len, max_query_len, &list);
+  const size_t slot_bytes = pa::prefill_slot_bytes(num_heads, head_dim);
+  const size_t slots = workspace ? workspace_bytes / slot_bytes : 0;
+  pa::SplitList split, merges;
+  const bool is_split =
+      listed && slots >= 2 &&
+      plan_prefill_split(list, num_heads, prefill_resident_groups(), slots, &split, &merges);
+  if (is_split) {
+    p.part_o = static_cast<float *>(workspace);
+    // [slots][H][128][D] outputs, then [slots][H][128] (max, sum)
+    const size_t o_bytes =
+        slots * (size_t)num_heads * pa::prefill_query_tile() * head_dim * sizeof(float);
+    p.part_ml = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + o_bytes);
+  }
+  pa::WorkList items;
+  if (listed && !is_split) {
+    items.count = (int)list.size();
+    for (size_t i = 0; i < list.size(); ++i) items.item[i] = list[i].code;
+  }
   return launch_checked("pa_prefill", [&] {
     return pa::launch_prefill(p, num_seqs, head_dim, block_size, max_query_len,
-                              listed ? &items : nullptr, static_cast<hipStream_t>(stream));
+                              listed && !is_split ? &items : nullptr, is_split ? &split : nullptr,
+                              is_split ? &merges : nullptr, static_cast<hipStream_t>(stream));
   });
 }
 

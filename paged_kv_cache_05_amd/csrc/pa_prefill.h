@@ -15,6 +15,11 @@ struct PrefillParams {
   const int32_t *block_tables;
   const int32_t *context_lens;
   const int32_t *query_start;     // [num_seqs + 1]
+  // Split launch only: partial results of key chunks, per slot
+  // [slot][head][128 rows][head_dim] fp32 (output before normalisation) and
+  // [slot][head][128 rows] (running max in log2 units, sum).
+  float *part_o;
+  float2 *part_ml;
   int num_heads;
   int num_blocks;
   int max_blocks_per_seq;
@@ -23,10 +28,30 @@ struct PrefillParams {
   float scale_log2;
 };
 
+// Launch list of the split form: each entry is one workgroup's (sequence,
+// query tile) and its key chunk; part = slot << 8 | chunk << 4 |
+// (chunks - 1) with the chunk's own workspace slot, 0 for a whole tile.  A
+// tile's chunks use consecutive slots.  The merge list holds one entry per
+// split tile: part = slot << 8 | (chunks - 1), slot being its first chunk's.
+constexpr int kMaxSplitItems = 448;
+constexpr int kMaxChunks = 16;
+struct SplitList {
+  int count;
+  uint32_t item[kMaxSplitItems];   // sequence << 16 | query tile
+  uint32_t part[kMaxSplitItems];
+};
+
 int prefill_query_tile();
+int prefill_key_tile();
+// Workspace bytes of one partial-result slot.
+size_t prefill_slot_bytes(int num_heads, int head_dim);
+// Workgroups of the prefill kernel that one CU holds at once.
+int prefill_groups_per_cu();
 // items: (sequence << 16 | query tile) in launch order, or nullptr for the
-// grid over (heads, tiles, sequences).
+// grid over (heads, tiles, sequences).  split / merges: the split form
+// (items unused).
 hipError_t launch_prefill(const PrefillParams &p, int num_seqs, int head_dim, int block_size,
-                          int max_query_len, const WorkList *items, hipStream_t stream);
+                          int max_query_len, const WorkList *items, const SplitList *split,
+                          const SplitList *merges, hipStream_t stream);
 
 }  // namespace pa

@@ -226,7 +226,11 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
 }
 
 template <int D, int B>
-__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds) {
+// With nchunks > 1 the workgroup covers key chunk `chunk` of the tile's
+// keys (an equal share of its 32-key tiles) and writes that chunk's partial
+// result to slot `slot` for the merge pass.
+__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds,
+                             int chunk = 0, int nchunks = 1, int slot = 0) {
   using G = Geo<D>;
   const int q0 = p.query_start[b];
   const int m = p.query_start[b + 1] - q0;
@@ -266,7 +270,11 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (kv_end > 0) stage_rows<D, B>(p, table, h, w, lane, kv_end, 0, lds, o);
+  // This workgroup's keys [k_lo, k_hi): all of them, or one chunk.
+  const int ntiles = (kv_end + kKeys - 1) / kKeys;
+  const int k_lo = (int)((int64_t)ntiles * chunk / nchunks) * kKeys;
+  const int k_hi = min(kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
+  if (k_lo < k_hi) stage_rows<D, B>(p, table, h, w, lane, kv_end, k_lo, lds, o);
   __builtin_amdgcn_s_waitcnt(0);   // query fragments and the first tile
   __syncthreads();
 
@@ -277,7 +285,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   auto step = [&](auto stage, int t0) {
     constexpr int kS = decltype(stage)::value;
     lds_char *cur = lds + kS * G::kStageBytes;
-    if (t0 + kKeys < kv_end)
+    if (t0 + kKeys < k_hi)
       stage_rows<D, B>(p, table, h, w, lane, kv_end, t0 + kKeys, lds + (kS ^ 1) * G::kStageBytes, o);
     if (wave_active && t0 <= wave_last) {
       const lds_char *ks = cur;
@@ -366,13 +374,28 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
   };
-  for (int t0 = 0; t0 < kv_end; t0 += 2 * kKeys) {
+  for (int t0 = k_lo; t0 < k_hi; t0 += 2 * kKeys) {
     step(std::integral_constant<int, 0>{}, t0);
-    if (t0 + kKeys >= kv_end) break;
+    if (t0 + kKeys >= k_hi) break;
     step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
 
   if (r >= m || q0 + r >= p.num_query_rows || q0 + r < 0) return;   // rows in range only
+  if (nchunks > 1) {
+    // Partial result: the unnormalised output and (m, l) of this chunk,
+    // for the merge pass; an empty chunk leaves m = -inf, l = 0, O = 0.
+    const size_t prow = ((size_t)slot * p.num_heads + h) * kQTile + w * kRows + c;
+    float *po = p.part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4 *>(po + dt * 32 + i4 * 8 + g * 4) =
+            make_float4(acc_o[dt][i4 * 4], acc_o[dt][i4 * 4 + 1], acc_o[dt][i4 * 4 + 2],
+                        acc_o[dt][i4 * 4 + 3]);
+    if (g == 0) p.part_ml[prow] = make_float2(m_run, l_run);
+    return;
+  }
   // Lane holds O^T[d][query c] for d = 32 dt + 8 (i/4) + 4 g + (i%4).
   const float inv = (bad_seq || !(l_run > 0.f)) ? NAN : 1.f / l_run;
   _Float16 *orow = static_cast<_Float16 *>(p.out) + ((int64_t)(q0 + r) * p.num_heads + h) * D;
@@ -414,9 +437,82 @@ prefill_listed_kernel(const PrefillParams p, const WorkList items) {
   prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds);
 }
 
+// grid (heads, split list entries): one key chunk of one query tile each.
+template <int D, int B>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
+prefill_split_kernel(const PrefillParams p, const SplitList items) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
+  const uint32_t it = items.item[blockIdx.y], part = items.part[blockIdx.y];
+  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds,
+                     (int)((part >> 4) & 15u), (int)(part & 15u) + 1, (int)(part >> 8));
+}
+
+// Merge of a split tile's chunks: grid (heads, split tiles), two threads per
+// query row, each over half the head dims.  The chunks' softmax states
+// combine by the usual rescaling: with M the largest running max,
+//   out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// Rows and invalid sequences follow the unsplit epilogue.
+template <int D>
+__global__ void __launch_bounds__(2 * kQTile) prefill_merge_kernel(const PrefillParams p,
+                                                                   const SplitList merges) {
+  constexpr int kSeg = D / 2;
+  const int h = blockIdx.x;
+  const uint32_t it = merges.item[blockIdx.y], part = merges.part[blockIdx.y];
+  const int b = (int)(it >> 16), qt = (int)(it & 0xffffu);
+  const int slot0 = (int)(part >> 8), nc = (int)(part & 15u) + 1;
+  const int q0 = p.query_start[b];
+  const int m = p.query_start[b + 1] - q0;
+  const int n = min(max(p.context_lens[b], 0), p.max_context_len);
+  const bool bad_seq = m < 0 || m > n || q0 < 0 || q0 + m > p.num_query_rows;
+  const int row = threadIdx.x >> 1, d0 = (threadIdx.x & 1) * kSeg;
+  const int r = qt * kQTile + row;
+  if (r >= m || q0 + r >= p.num_query_rows || q0 + r < 0) return;
+  float M = -INFINITY;
+  for (int i = 0; i < nc; ++i)
+    M = fmaxf(M, p.part_ml[((size_t)(slot0 + i) * p.num_heads + h) * kQTile + row].x);
+  float L = 0.f, acc[kSeg];
+#pragma unroll
+  for (int e = 0; e < kSeg; ++e) acc[e] = 0.f;
+  for (int i = 0; i < nc; ++i) {
+    const size_t prow = ((size_t)(slot0 + i) * p.num_heads + h) * kQTile + row;
+    const float2 ml = p.part_ml[prow];
+    const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    L += wgt * ml.y;
+    const float4 *po = reinterpret_cast<const float4 *>(p.part_o + prow * D + d0);
+#pragma unroll
+    for (int e = 0; e < kSeg / 4; ++e) {
+      const float4 v = po[e];
+      acc[4 * e] += wgt * v.x;
+      acc[4 * e + 1] += wgt * v.y;
+      acc[4 * e + 2] += wgt * v.z;
+      acc[4 * e + 3] += wgt * v.w;
+    }
+  }
+  const float inv = (bad_seq || !(L > 0.f)) ? NAN : 1.f / L;
+  _Float16 *orow =
+      static_cast<_Float16 *>(p.out) + ((int64_t)(q0 + r) * p.num_heads + h) * D + d0;
+#pragma unroll
+  for (int e = 0; e < kSeg / 4; ++e) {
+    half4 o4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o4[k] = (_Float16)(acc[4 * e + k] * inv);
+    *reinterpret_cast<half4 *>(orow + 4 * e) = o4;
+  }
+}
+
 template <int D, int B>
 hipError_t launch_db(const PrefillParams &p, int num_seqs, int max_query_len,
-                     const WorkList *items, hipStream_t stream) {
+                     const WorkList *items, const SplitList *split, const SplitList *merges,
+                     hipStream_t stream) {
+  if (split) {
+    if (split->count > 0)
+      prefill_split_kernel<D, B>
+          <<<dim3(p.num_heads, split->count), kThreads, 0, stream>>>(p, *split);
+    if (merges && merges->count > 0)
+      prefill_merge_kernel<D>
+          <<<dim3(p.num_heads, merges->count), 2 * kQTile, 0, stream>>>(p, *merges);
+    return hipGetLastError();
+  }
   if (items) {
     if (items->count > 0)
       prefill_listed_kernel<D, B>
@@ -430,12 +526,13 @@ hipError_t launch_db(const PrefillParams &p, int num_seqs, int max_query_len,
 
 template <int D>
 hipError_t launch_d(const PrefillParams &p, int num_seqs, int block_size, int max_query_len,
-                    const WorkList *items, hipStream_t stream) {
+                    const WorkList *items, const SplitList *split, const SplitList *merges,
+                    hipStream_t stream) {
   switch (block_size) {
-    case 8: return launch_db<D, 8>(p, num_seqs, max_query_len, items, stream);
-    case 16: return launch_db<D, 16>(p, num_seqs, max_query_len, items, stream);
-    case 32: return launch_db<D, 32>(p, num_seqs, max_query_len, items, stream);
-    case 64: return launch_db<D, 64>(p, num_seqs, max_query_len, items, stream);
+    case 8: return launch_db<D, 8>(p, num_seqs, max_query_len, items, split, merges, stream);
+    case 16: return launch_db<D, 16>(p, num_seqs, max_query_len, items, split, merges, stream);
+    case 32: return launch_db<D, 32>(p, num_seqs, max_query_len, items, split, merges, stream);
+    case 64: return launch_db<D, 64>(p, num_seqs, max_query_len, items, split, merges, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -443,11 +540,23 @@ hipError_t launch_d(const PrefillParams &p, int num_seqs, int block_size, int ma
 }  // namespace
 
 int prefill_query_tile() { return kQTile; }
+int prefill_key_tile() { return kKeys; }
+
+size_t prefill_slot_bytes(int num_heads, int head_dim) {
+  return (size_t)num_heads * kQTile * ((size_t)head_dim * sizeof(float) + sizeof(float2));
+}
+
+// 168 VGPRs per wave: three waves per SIMD, so three 4-wave workgroups per
+// CU (their 32 KB of LDS each fits as well).
+int prefill_groups_per_cu() { return 3; }
 
 hipError_t launch_prefill(const PrefillParams &p, int num_seqs, int head_dim, int block_size,
-                          int max_query_len, const WorkList *items, hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(p, num_seqs, block_size, max_query_len, items, stream);
-  if (head_dim == 64) return launch_d<64>(p, num_seqs, block_size, max_query_len, items, stream);
+                          int max_query_len, const WorkList *items, const SplitList *split,
+                          const SplitList *merges, hipStream_t stream) {
+  if (head_dim == 128)
+    return launch_d<128>(p, num_seqs, block_size, max_query_len, items, split, merges, stream);
+  if (head_dim == 64)
+    return launch_d<64>(p, num_seqs, block_size, max_query_len, items, split, merges, stream);
   return hipErrorInvalidValue;
 }
 

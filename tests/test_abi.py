@@ -153,7 +153,7 @@ def prefill_call(lib, **over):
                 query_start=CL, num_seqs=4, num_query_rows=40, num_heads=2, head_dim=64,
                 block_size=16, num_blocks=32, max_blocks_per_seq=4, max_context_len=50,
                 max_query_len=20, scale=0.125, dtype=0, host_query_start=None,
-                host_context_lens=None, stream=None)
+                host_context_lens=None, workspace=None, workspace_bytes=0, stream=None)
     args.update(over)
     return lib.pa_prefill(*args.values())
 
@@ -168,6 +168,7 @@ def prefill_call(lib, **over):
     (dict(q=Q + 8), -2), (dict(query_start=CL + 2), -2), (dict(num_seqs=70000), -2),
     (dict(num_seqs=0, out=None), 0), (dict(num_query_rows=0, q=None), 0),
     (dict(max_query_len=0, out=None), 0),
+    (dict(workspace=WS + 8, workspace_bytes=1 << 20), -2),
 ])
 def test_prefill_rejects(pa, over, code):
     assert prefill_call(pa.library(), **over) == code
@@ -234,3 +235,12 @@ def test_one_hip_runtime_whatever_the_import_order():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_prefill_workspace_bytes(pa):
+    """slots x heads x 128 query rows x (head_dim fp32 outputs + (max, sum))."""
+    lib = pa.library()
+    assert lib.pa_prefill_workspace_bytes(40, 128, 64) == 64 * 40 * 128 * (128 * 4 + 8)
+    assert lib.pa_prefill_workspace_bytes(2, 64, 1) == 2 * 128 * (64 * 4 + 8)
+    for bad in ((0, 128, 4), (40, 96, 4), (40, 128, 0), (40, 128, -1)):
+        assert lib.pa_prefill_workspace_bytes(*bad) == 0

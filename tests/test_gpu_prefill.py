@@ -171,6 +171,109 @@ def test_prefill_rows_before_zero_are_not_written(pa, oracle_lib, device):
     check(got[pad + n0:], ref[n0:], "other sequence")
 
 
+def run_split(pa, wl, device, slots, tables=None, context_lens=None):
+    """The listed launch with a workspace of `slots` partial-result slots,
+    pre-filled with a byte pattern; also says whether the launch wrote to it
+    (the split form ran)."""
+    T, H, D = wl.q.shape
+    ctx = wl.context_lens if context_lens is None else context_lens
+    ws = torch.full((pa.pa_prefill_workspace_bytes(H, D, slots),), 0x5A, dtype=torch.uint8,
+                    device=device)
+    dq = dev(wl.q, device)
+    out = torch.full_like(dq, float("nan"))
+    pa.pa_prefill(out, dq, dev(wl.k_pool, device), dev(wl.v_pool, device),
+                  dev(wl.block_tables if tables is None else tables, device), dev(ctx, device),
+                  dev(wl.query_start, device), float(wl.scale), max(int(np.max(ctx)), 1),
+                  int(np.diff(wl.query_start).max()), host_query_start=wl.query_start,
+                  host_context_lens=ctx, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), bool((ws != 0x5A).any().item())
+
+
+SPLIT_CASES = {
+    # few heads and query tiles of at least 48 key tiles (1536 keys), so the
+    # planner splits the heaviest tiles over the idle GPU
+    "one-prompt-b16-d128": lambda: W.prefill_small(seed=21, head_dim=128,
+                                                   groups=((0, [1700]),)),
+    "suffix-b16-d64": lambda: W.prefill_small(seed=22, groups=((1700, [100]), (0, [5]))),
+    "one-prompt-b8-d128": lambda: W.prefill_small(seed=23, head_dim=128, block_size=8,
+                                                  groups=((0, [1600]),)),
+    "one-prompt-b64-d64": lambda: W.prefill_small(seed=24, block_size=64,
+                                                  groups=((0, [1650]),)),
+    "suffixes-b32-d128": lambda: W.prefill_small(seed=25, head_dim=128, block_size=32,
+                                                 groups=((1600, [1, 300]), (0, [40]))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_CASES))
+def test_prefill_split_matches_oracle(pa, oracle_lib, device, name):
+    """With a workspace the heaviest query tiles are split into key chunks
+    and merged: oracle parity, and the workspace was used."""
+    announce(f"prefill split {name}")
+    wl = SPLIT_CASES[name]()
+    got, used = run_split(pa, wl, device, slots=64)
+    assert used, "the split form did not run"
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(got, ref, name)
+
+
+def test_prefill_split_with_few_slots(pa, oracle_lib, device):
+    """Two slots: only the heaviest tile is split, the rest run whole."""
+    announce("prefill split, two slots")
+    wl = SPLIT_CASES["one-prompt-b16-d128"]()
+    got, used = run_split(pa, wl, device, slots=2)
+    assert used
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(got, ref, "two slots")
+
+
+def test_prefill_split_poisons_rows_that_see_a_bad_block(pa, oracle_lib, device):
+    """A bad table entry inside a split tile's key range: exactly the rows
+    that see it are NaN after the merge."""
+    announce("prefill split, bad table entry")
+    wl = SPLIT_CASES["one-prompt-b16-d128"]()
+    B = wl.block_size
+    tables = wl.block_tables.copy()
+    tables[0, 20] = -7                           # keys 320..335
+    got, used = run_split(pa, wl, device, slots=64, tables=tables)
+    assert used
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    n0 = int(wl.context_lens[0])
+    sees = np.arange(n0) >= 20 * B
+    assert np.isnan(got[:n0][sees]).all()
+    check(got[:n0][~sees], ref[:n0][~sees], "rows before the bad block")
+
+
+def test_prefill_split_invalid_chunk_is_nan(pa, oracle_lib, device):
+    """A sequence with more queries than context tokens gets NaN rows in the
+    split form too; the other sequence is unaffected."""
+    announce("prefill split, invalid chunk")
+    wl = SPLIT_CASES["suffix-b16-d64"]()
+    ctx = wl.context_lens.copy()
+    ctx[1] = 2                                   # 5 queries over 2 tokens
+    got, used = run_split(pa, wl, device, slots=64, context_lens=ctx)
+    assert used
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    n0 = int(wl.query_start[1])
+    check(got[:n0], ref[:n0], "valid sequence")
+    assert np.isnan(got[n0:]).all()
+
+
+def test_prefill_no_split_when_balanced(pa, oracle_lib, device):
+    """A batch whose work spreads over the GPU is not split even with a
+    workspace: the output is bit for bit the listed launch's."""
+    announce("prefill no split when balanced")
+    wl = W.prefill_mix(seed=8, num_heads=40, num_seqs=24, hi=300)
+    got, used = run_split(pa, wl, device, slots=64)
+    assert not used
+    listed = run_gpu(pa, wl, device, listed=True)
+    assert np.array_equal(got.view(np.uint16), listed.view(np.uint16))
+
+
 def sampled_rows(wl, per_seq, rng):
     """(sequence, first row, count) windows whose oracle values need only a
     truncated context: a query at position p sees tokens 0..p."""
