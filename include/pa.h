@@ -134,7 +134,11 @@ int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int
  *                  merges only the sequences that span several partitions
  *                  (up to 960 items; beyond that, and without it, one
  *                  workgroup per (head, sequence, partition) is launched
- *                  and empty ones leave at once).  Each entry must be at
+ *                  and empty ones leave at once).  When the mean item is
+ *                  shorter than 192 tokens, those workgroups have 4 waves
+ *                  (2 at block size 8) instead of 8; the result then
+ *                  differs from the unplanned launch's by fp32 rounding
+ *                  order, otherwise it is the same bit for bit.  Each entry must be at
  *                  least the device value it copies (equal for the best
  *                  schedule); the device values still decide every result.
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)

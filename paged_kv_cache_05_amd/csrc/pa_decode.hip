@@ -515,20 +515,31 @@ __global__ void __launch_bounds__(D) merge_listed_kernel(const DecodeParams p,
   merge_one<T, D>(p, blockIdx.x, (int)rows.item[blockIdx.y]);
 }
 
-// Waves per workgroup: 8 (4 and 16 measured slower).
+// Waves per workgroup of the grid launch: 8 (4 and 16 measured slower on
+// the lognormal batch).  The listed launch also has 2- and 4-wave forms for
+// batches of short rows, where 8 waves leave most of them one tile or none.
 constexpr int kDecodeWaves = 8;
 
 struct Lists {
   const WorkList *items, *merge_rows;
+  int waves;
 };
+
+template <typename T, int D, int B, int W>
+void launch_listed(const DecodeParams &p, Lists l, hipStream_t stream) {
+  decode_listed_kernel<T, D, B, W>
+      <<<dim3(p.num_heads, l.items->count), 64 * W, 0, stream>>>(p, *l.items);
+}
 
 template <typename T, int D, int B>
 hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_t stream) {
   constexpr int W = kDecodeWaves;
   if (l.items) {
-    if (l.items->count > 0)
-      decode_listed_kernel<T, D, B, W>
-          <<<dim3(p.num_heads, l.items->count), 64 * W, 0, stream>>>(p, *l.items);
+    if (l.items->count > 0) {
+      if (l.waves == 2) launch_listed<T, D, B, 2>(p, l, stream);
+      else if (l.waves == 4) launch_listed<T, D, B, 4>(p, l, stream);
+      else launch_listed<T, D, B, 8>(p, l, stream);
+    }
     if (p.num_partitions > 1 && l.merge_rows && l.merge_rows->count > 0)
       merge_listed_kernel<T, D>
           <<<dim3(p.num_heads, l.merge_rows->count), D, 0, stream>>>(p, *l.merge_rows);
@@ -580,8 +591,8 @@ WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_di
 
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
                          int dtype, const WorkList *items, const WorkList *merge_rows,
-                         hipStream_t stream) {
-  const Lists l{items, merge_rows};
+                         int waves, hipStream_t stream) {
+  const Lists l{items, merge_rows, waves};
   if (dtype == 0) return launch_dim<_Float16>(p, num_seqs, head_dim, block_size, l, stream);
   if (dtype == 1) return launch_dim<float>(p, num_seqs, head_dim, block_size, l, stream);
   return hipErrorInvalidValue;

@@ -327,6 +327,13 @@ def test_write_skips_slots_outside_pool(pa, oracle_lib, device):
     assert np.array_equal(tbits(k), bits(ok)) and np.array_equal(tbits(v), bits(ov))
 
 
+def planned_waves(ctx, part, block_size):
+    """The planner's waves per workgroup: 4 (2 at B = 8) when the mean
+    (sequence, partition) item is shorter than 12 tiles of 16 tokens."""
+    items = sum(1 if c == 0 else -(-int(c) // part) for c in ctx)
+    return 8 if items * 12 * 16 <= int(np.sum(ctx)) else (2 if block_size == 8 else 4)
+
+
 @pytest.mark.parametrize("config,kw,part", [
     (1, {}, 16), (1, {}, 0), (2, {}, 0), (2, {}, 256), (2, {}, 1024), (3, {"block_size": 8}, 0),
     (3, {"block_size": 32}, 64), (4, {}, 0), (4, {}, 128),
@@ -336,17 +343,33 @@ def test_write_skips_slots_outside_pool(pa, oracle_lib, device):
 def test_host_planned_launch(pa, oracle_lib, device, config, kw, part):
     """With host-side context lengths the library launches only the non-empty
     (sequence, partition) items, long ones first.  With an explicit partition
-    size the results are bit-identical to the unplanned launch (same
-    per-partition reduction order); with partition_size 0 the library also
-    picks the partition size from the lengths."""
+    size and 8-wave workgroups the results are bit-identical to the unplanned
+    launch (same per-partition reduction order); with partition_size 0 the
+    library also picks the partition size from the lengths."""
     wl = workload(config, **kw)
     k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
     announce(f"{wl.name}: planned vs unplanned, partition {part}")
     plain = gpu_decode(pa, wl, k, v, device, partition_size=part)
     planned = gpu_decode(pa, wl, k, v, device, partition_size=part, host_ctx=wl.context_lens)
-    if part:
+    if part and planned_waves(wl.context_lens, part, wl.block_size) == 8:
         assert np.array_equal(bits(planned), bits(plain))
     assert_close(planned, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
+
+
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+def test_short_rows_use_fewer_waves(pa, oracle_lib, device, B):
+    """Batches of short rows (mean item under 192 tokens) run the planned
+    launch with 4 waves per workgroup (2 at B = 8): oracle parity at every
+    block size, fp16 and fp32, including one-token rows and ragged tails."""
+    for dtype in (W.F16, W.F32):
+        ctx = np.random.default_rng(40 + B).integers(1, 180, size=96)
+        ctx[:3] = (1, 2, 17)
+        wl = W._simple(f"short-rows-b{B}", 40 + B, dtype, 8, 128 if dtype == W.F16 else 64, B, ctx)
+        assert planned_waves(ctx, 4096, B) in (2, 4)
+        announce(f"{wl.name} {dtype}: planned short-row launch")
+        got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
+                         host_ctx=wl.context_lens)
+        assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
 
 
 def test_host_lengths_as_upper_bound(pa, oracle_lib, device):
