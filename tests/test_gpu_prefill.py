@@ -304,3 +304,49 @@ def test_prefill_full_size_sampled(pa, oracle_lib, device, which):
                                  wl.block_tables[b:b + 1], np.array([n_cut], np.int32),
                                  np.array([0, k], np.int32), wl.scale)
         check(got[qs + s:qs + s + k], ref, f"sequence {b} rows {s}..{s + k - 1}")
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["listed", "split"])
+def test_prefill_replayed_from_a_hip_graph(pa, oracle_lib, device, split):
+    """pa_prefill (listed, and split with its merge pass) captured once and
+    replayed three times, with eager work and synchronisation between
+    replays: every replay reproduces the eager result bit for bit."""
+    wl = SPLIT_CASES["suffix-b16-d64"]()
+    T, H, D = wl.q.shape
+    q, kp, vp = dev(wl.q, device), dev(wl.k_pool, device), dev(wl.v_pool, device)
+    tb, cx, qs = dev(wl.block_tables, device), dev(wl.context_lens, device), dev(wl.query_start, device)
+    ws = (torch.empty(pa.pa_prefill_workspace_bytes(H, D, 64), dtype=torch.uint8, device=device)
+          if split else None)
+    out = torch.empty_like(q)
+
+    def call():
+        pa.pa_prefill(out, q, kp, vp, tb, cx, qs, float(wl.scale), wl.max_context_len,
+                      wl.max_query_len, host_query_start=wl.query_start,
+                      host_context_lens=wl.context_lens, workspace=ws)
+
+    announce(f"prefill eager ({'split' if split else 'listed'})")
+    call()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy()
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(eager, ref, "eager")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    announce("prefill capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))          # eager work between replays
+        if ws is not None:
+            ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        announce(f"prefill replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager.view(np.uint16)), \
+            f"replay {r}: output differs"
