@@ -263,6 +263,32 @@ def test_prefill_split_invalid_chunk_is_nan(pa, oracle_lib, device):
     assert np.isnan(got[n0:]).all()
 
 
+def test_prefill_split_with_empty_chunks(pa, oracle_lib, device):
+    """Host context lengths are upper bounds: planned from a 1740-token
+    context, the device one is 50, so the tile's key range (2 tiles) is
+    shorter than its chunk count and some chunks are empty (max -inf, sum
+    0); the merge still gives the oracle's rows."""
+    announce("prefill split, empty chunks")
+    wl = W.prefill_small(seed=26, head_dim=128, groups=((1700, [40]),))
+    T, H, D = wl.q.shape
+    host_ctx = wl.context_lens.copy()
+    ctx = wl.context_lens.copy()
+    ctx[0] = 50                                  # the 40 queries sit at positions 10..49
+    ws = torch.full((pa.pa_prefill_workspace_bytes(H, D, 64),), 0x5A, dtype=torch.uint8,
+                    device=device)
+    dq = dev(wl.q, device)
+    out = torch.full_like(dq, float("nan"))
+    pa.pa_prefill(out, dq, dev(wl.k_pool, device), dev(wl.v_pool, device),
+                  dev(wl.block_tables, device), dev(ctx, device), dev(wl.query_start, device),
+                  float(wl.scale), int(host_ctx.max()), 40, host_query_start=wl.query_start,
+                  host_context_lens=host_ctx, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws != 0x5A).any().item()), "the split form did not run"
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, ctx,
+                             wl.query_start, wl.scale)
+    check(out.cpu().numpy(), ref, "empty chunks")
+
+
 def test_prefill_no_split_when_balanced(pa, oracle_lib, device):
     """A batch whose work spreads over the GPU is not split even with a
     workspace: the output is bit for bit the listed launch's."""
