@@ -47,27 +47,30 @@ PEAK_HBM_GBS = 8000.0
 COUNTER_FILE = os.path.join(ROOT, "profiles", "pa_decode_opt13b_hbm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_05_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_kernels.h")]
+PREFILL_COUNTER_FILE = os.path.join(ROOT, "profiles", "pa_prefill_opt13b_hbm_counters.txt")
+PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_05_amd", "csrc", f)
+                   for f in ("pa_prefill.hip", "pa_prefill.h", "pa_kernels.h")]
 
 
-def kernel_digest():
+def kernel_digest(sources=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES if sources is None else sources:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed rocprofv3 counter runs
+def measured_traffic(counter_file=COUNTER_FILE, sources=None):
+    """HBM bytes per call from the committed rocprofv3 counter runs
     (``key: value`` lines), if they were taken on the kernel source as it is
     now; otherwise None."""
     try:
-        with open(COUNTER_FILE) as f:
+        with open(counter_file) as f:
             c = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
     c = {k.strip(): v.strip() for k, v in c.items()}
-    if c.get("kernel_digest") != kernel_digest():
+    if c.get("kernel_digest") != kernel_digest(sources):
         return None
     try:
         return int(c["hbm_bytes_per_call"])
@@ -208,7 +211,8 @@ def bench_prefill(args):
         "roofline": {"bound": "mfma", "achieved": round(launch_tflops, 2),
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(launch_tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": None, "kernel": "prefill_listed_kernel<128,16>",
+                     "traffic": measured_traffic(PREFILL_COUNTER_FILE, PREFILL_SOURCES),
+                     "kernel": "prefill_listed_kernel<128,16>",
                      "from": "algorithmic FLOPs / mean event span of one call"},
         "hbm_GBps_algorithmic": round(mix["bytes"] / (mix["ms"] * 1e-3) / 1e9, 1),
         "ms_per_call_events": round(mix["per_call"], 5),
