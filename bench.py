@@ -174,7 +174,7 @@ def bench_prefill(args):
     launch_tflops = mix["flops"] / (mix["per_call"] * 1e-3) / 1e12
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and default_config:
         import oracle
         if not os.path.exists(oracle.LIBRARY):
             oracle.build()
@@ -472,6 +472,13 @@ def main():
                          "pa_decode_append")
     ap.add_argument("--no-host-lengths", action="store_true",
                     help="do not pass host-side context lengths to pa_decode")
+    ap.add_argument("--config", choices=["opt13b", "short", "long"], default="opt13b",
+                    help="decode workload: opt13b (the default line: 64 seqs x 40 heads, "
+                         "lognormal contexts), short (256 seqs of 20-200 tokens), long (32 seqs "
+                         "x 96 heads of 4096-16384 tokens); the CPU baseline and the stored HBM "
+                         "counters cover opt13b only")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
+                    help="block size of the short workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run one 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--workload", choices=["decode", "generation", "beam", "swap", "prefill"],
@@ -502,9 +509,16 @@ def main():
     import workloads as W
 
     device = torch.device("cuda:0")
-    wl = W.config2(host=False)
+    # The default line is the OPT-13B-shaped layer; the other decode
+    # workloads are the short-request batch (any block size) and the
+    # long-context OPT-175B-shaped layer, whose pools (24 GB each) already
+    # dwarf the caches, so two of them rotate.
+    wl = {"opt13b": lambda: W.config2(host=False),
+          "short": lambda: W.config3(block_size=args.block_size, host=False),
+          "long": lambda: W.config5(host=False)}[args.config]()
     N, H, D, B = wl.num_seqs, wl.num_heads, wl.head_dim, wl.block_size
-    L = args.layers
+    L = min(args.layers, 2) if args.config == "long" else args.layers
+    default_config = args.config == "opt13b"
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
     pools = [W.device_pools(wl, device, seed_offset=layer) for layer in range(L)]
     tables, ctx = dev(wl.block_tables), dev(wl.context_lens)
@@ -521,8 +535,11 @@ def main():
     part = pa.pa_decode_partition_size(N, H, D, maxctx, args.partition, host_ctx,
                                        ws.numel() if ws is not None else 0)
     merges = -(-maxctx // part) > 1
+    # Waves per workgroup: 8 for the default workload; the planner may pick
+    # fewer for batches of short rows, shown as W.
+    waves = "8" if default_config or host_ctx is None else "W"
     kernel = ("decode_listed_kernel" if host_ctx is not None else "decode_kernel") + \
-        f"<{'f16' if wl.dtype == W.F16 else 'f32'},{D},{B},8>" + \
+        f"<{'f16' if wl.dtype == W.F16 else 'f32'},{D},{B},{waves}>" + \
         (" + merge_kernel" if merges else "") + \
         ("" if args.split_step else " (fused append: pa_decode_append)")
     stream = torch.cuda.current_stream()
@@ -598,7 +615,8 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_mean = float(dec_ms.mean())
     achieved = call_bytes / (dec_mean * 1e-3) / 1e9
-    traffic = None if args.split_step else measured_traffic()
+    # the stored counters cover the default workload's fused call only
+    traffic = None if args.split_step or not default_config else measured_traffic()
 
     # Output of layer 0 for the parity sample and the CPU baseline.
     k0, v0 = pools[0]
@@ -610,7 +628,7 @@ def main():
 
     cpu = None
     parity = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and default_config:
         import oracle
         if not os.path.exists(oracle.LIBRARY):
             oracle.build()
@@ -640,11 +658,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded; lognormal context lengths, N(0,1) q/K/V, scattered blocks)",
+        "data": "synthetic (seeded context lengths, N(0,1) q/K/V, scattered blocks)",
         "config": {
-            "workload": "OPT-13B-shaped single-layer decode step (new-token store + paged decode)",
+            "workload": {"opt13b": "OPT-13B-shaped single-layer decode step",
+                         "short": "short-request high-batch decode step",
+                         "long": "long-context OPT-175B-shaped single-layer decode step"}[
+                             args.config] + " (new-token store + paged decode)",
             "num_seqs": N, "num_heads": H, "head_dim": D, "block_size": B,
-            "context_lens": "lognormal median 300 sigma 0.9 clipped [1,2048]",
+            "context_lens": {"opt13b": "lognormal median 300 sigma 0.9 clipped [1,2048]",
+                             "short": "uniform [20,200]",
+                             "long": "uniform [4096,16384]"}[args.config],
             "sum_context": int(wl.context_lens.sum()), "max_context": maxctx,
             "num_blocks": wl.num_blocks, "layer_pools_rotated": L,
             "partition_size": part,

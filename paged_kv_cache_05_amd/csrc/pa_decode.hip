@@ -49,6 +49,8 @@ namespace pa {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// An int32 in the constant address space (read-only for the kernel's life).
+typedef const __attribute__((address_space(4))) int32_t ConstI32;
 
 union Chunk {  // one 16-byte vector load
   uint4 u;
@@ -192,7 +194,15 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
     for (int k = 0; k < G::kChunksPerLane; ++k) qc[k] = load_chunk(qp + (col + k * kLPT) * 16);
   }
 
+  // Two views of the sequence's table row.  Inside the tile loop entries are
+  // read through the constant address space: the kernel never writes the
+  // tables, and a constant load at a wave-uniform address becomes a scalar
+  // load whose wait (lgkmcnt) leaves the prefetched K/V loads in flight,
+  // where a vector load would need vmcnt(0), which retires in order.  A
+  // wave's first tile and the ragged tile have nothing else in flight, and
+  // there the vector path's shorter latency wins.
   const int32_t *table = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const ConstI32 *table_s = (const ConstI32 *)table;
   const size_t block_bytes = (size_t)H * B * D * sizeof(T);
   const size_t lane_off = ((size_t)h * B + trow) * D * sizeof(T) + (size_t)col * 16;
   const char *kbase = reinterpret_cast<const char *>(p.k_pool) + lane_off;
@@ -209,9 +219,10 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
 
   // Load the 16-token tile starting at logical token ts.  With kCheck,
   // groups at or past tok_end are not loaded (their table entries may not
-  // exist); full tiles skip the check.
-  auto fetch = [&](Tile<T, D> &tile, int ts, auto check_tag) {
+  // exist); full tiles skip the check.  kScalar picks the table view.
+  auto fetch = [&](Tile<T, D> &tile, int ts, auto check_tag, auto scalar_tag) {
     constexpr bool kCheck = decltype(check_tag)::value;
+    constexpr bool kScalar = decltype(scalar_tag)::value;
 #pragma unroll
     for (int g = 0; g < G::kGroups; ++g) {
       const int gs = ts + g * kTPG;
@@ -224,21 +235,24 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
         off = gs % B;
       }
       if (!kCheck || gs < tok_end) {
-        const int phys = table[lb];
+        const int phys = kScalar ? table_s[lb] : table[lb];
         const bool ok = (unsigned)phys < num_blocks;
         bad |= !ok;
         const size_t boff = (size_t)(ok ? phys : 0) * block_bytes + (size_t)off * D * sizeof(T);
+        // The lanes of the appended token read its new rows instead: one
+        // load per chunk either way, so no second write to the tile
+        // registers is pending when the tile is consumed.
+        const bool fresh = append && gs + trow == last;
 #pragma unroll
         for (int k = 0; k < G::kChunksPerLane; ++k) {
-          tile.k[g][k] = load_stream(kbase + boff + k * kLPT * 16);
-          tile.v[g][k] = load_stream(vbase + boff + k * kLPT * 16);
-        }
-        if (append && ts <= last && last < ts + G::kTile && gs + trow == last) {
-#pragma unroll
-          for (int k = 0; k < G::kChunksPerLane; ++k) {
-            tile.k[g][k] = load_chunk(nk + (col + k * kLPT) * 16);
-            tile.v[g][k] = load_chunk(nv + (col + k * kLPT) * 16);
+          const char *ka = kbase + boff + k * kLPT * 16;
+          const char *va = vbase + boff + k * kLPT * 16;
+          if (fresh) {
+            ka = nk + (col + k * kLPT) * 16;
+            va = nv + (col + k * kLPT) * 16;
           }
+          tile.k[g][k] = load_stream(ka);
+          tile.v[g][k] = load_stream(va);
         }
       } else {
 #pragma unroll
@@ -309,30 +323,29 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
     // wait before a consume covers only that tile's loads.
     const int iters = nfull > wave ? (nfull - wave + W - 1) / W : 0;
     Tile<T, D> ta, tb;
-    int t = wave;
-    if (iters > 0) fetch(ta, tok0 + t * G::kTile, std::false_type());
-    for (int i = 0; i < iters; i += 2) {
-      if (i + 1 < iters) {
-        fetch(tb, tok0 + (t + W) * G::kTile, std::false_type());
-        consume(ta, tok0 + t * G::kTile, std::false_type());
-      } else {
-        consume(ta, tok0 + t * G::kTile, std::false_type());
-        break;
-      }
-      t += W;
-      if (i + 2 < iters) {
-        fetch(ta, tok0 + (t + W) * G::kTile, std::false_type());
-        consume(tb, tok0 + t * G::kTile, std::false_type());
-      } else {
-        consume(tb, tok0 + t * G::kTile, std::false_type());
-        break;
-      }
-      t += W;
+    auto tile_start = [&](int n) { return tok0 + (wave + n * W) * G::kTile; };
+    if (iters > 0) fetch(ta, tile_start(0), std::false_type(), std::false_type());
+    int n = 0;
+    for (; n + 2 < iters; n += 2) {
+      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type());
+      __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads first
+      consume(ta, tile_start(n), std::false_type());
+      fetch(ta, tile_start(n + 2), std::false_type(), std::true_type());
+      __builtin_amdgcn_sched_barrier(0);
+      consume(tb, tile_start(n + 1), std::false_type());
+    }
+    if (n + 1 < iters) {
+      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type());
+      __builtin_amdgcn_sched_barrier(0);
+      consume(ta, tile_start(n), std::false_type());
+      consume(tb, tile_start(n + 1), std::false_type());
+    } else if (n < iters) {
+      consume(ta, tile_start(n), std::false_type());
     }
     // Ragged last tile.
     if (nfull * G::kTile < span && wave == nfull % W) {
       const int ts = tok0 + nfull * G::kTile;
-      fetch(ta, ts, std::true_type());
+      fetch(ta, ts, std::true_type(), std::false_type());
       consume(ta, ts, std::true_type());
     }
   }
