@@ -499,6 +499,26 @@ def test_decode_append_equals_write_then_decode(pa, oracle_lib, device, config, 
                      "fused vs oracle")
 
 
+@pytest.mark.parametrize("part,host", [(0, False), (0, True), (16, True), (64, False)])
+def test_decode_append_full_last_tile(pa, device, part, host):
+    """Contexts that end exactly on a 16-token tile: the tile holding the new
+    token is full, and the fused step must still match the write followed by
+    the decode bit for bit (pools and outputs)."""
+    wl = workload(2)
+    ctx = wl.context_lens.copy()
+    ctx = np.where(ctx >= 16, ctx // 16 * 16, ctx).astype(ctx.dtype)
+    assert np.sum(ctx % 16 == 0) > len(ctx) // 2
+    B = wl.block_size
+    last = ctx - 1
+    slots = (wl.block_tables[np.arange(len(ctx)), last // B].astype(np.int64) * B
+             + last % B).astype(np.int64)
+    announce(f"decode_append full last tile part={part} host={host}")
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, part, host, ctx=ctx,
+                                                 slots=slots)
+    assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    assert np.array_equal(fo, so)
+
+
 def test_decode_append_empty_context_still_writes(pa, device):
     """A sequence with context 0 gets a zero row and its new token is still
     stored (as pa_write_kv would)."""
