@@ -502,6 +502,7 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
   p.v_pool = v_pool;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;

@@ -52,6 +52,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // An int32 in the constant address space (read-only for the kernel's life).
 typedef const __attribute__((address_space(4))) int32_t ConstI32;
 
+// 16-byte chunks each writer thread of a fused append copies (its loads are
+// issued together, then its stores).
+constexpr int kWriterChunks = 4;
+
 union Chunk {  // one 16-byte vector load
   uint4 u;
   uint32_t w[4];
@@ -444,17 +448,67 @@ __device__ __forceinline__ void store_new_token(const DecodeParams &p, int b, in
   }
 }
 
+// Fused append in the listed launch: workgroups past the list copy the new
+// tokens' K and V rows of head h, sequences [first, first + count), to their
+// slots (slots outside the pool are skipped, as pa_write_kv does).  No
+// workgroup of the launch reads those slots: the attention takes the new
+// token from its input rows.
 template <typename T, int D, int B, int W>
+__device__ __forceinline__ void write_new_rows(const DecodeParams &p, int h, int first,
+                                               int count) {
+  constexpr int kC = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  constexpr int kThreads = 64 * W;
+  // Three phases (slots, rows, stores), so each phase's loads are in flight
+  // together: two memory latencies per writer, not two per chunk.
+  int64_t slot[kWriterChunks];
+#pragma unroll
+  for (int i = 0; i < kWriterChunks; ++i) {
+    const int c = (int)threadIdx.x + i * kThreads;
+    slot[i] = c < count * 2 * kC ? p.slot_mapping[first + c / (2 * kC)] : -1;
+  }
+  uint4 data[kWriterChunks];
+  uint4 *dst[kWriterChunks];
+#pragma unroll
+  for (int i = 0; i < kWriterChunks; ++i) {
+    const int c = (int)threadIdx.x + i * kThreads;
+    dst[i] = nullptr;
+    data[i] = make_uint4(0, 0, 0, 0);
+    if (slot[i] >= 0 && slot[i] < (int64_t)p.num_blocks * B) {
+      const int b = first + c / (2 * kC);
+      const int e = c % (2 * kC);
+      const bool is_k = e < kC;
+      const int ch = is_k ? e : e - kC;
+      const size_t src = ((size_t)b * p.num_heads + h) * kC + ch;
+      const size_t at =
+          (((size_t)(slot[i] / B) * p.num_heads + h) * B + (size_t)(slot[i] % B)) * kC + ch;
+      data[i] = reinterpret_cast<const uint4 *>(is_k ? p.new_key : p.new_value)[src];
+      dst[i] = reinterpret_cast<uint4 *>(const_cast<void *>(is_k ? p.k_pool : p.v_pool)) + at;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kWriterChunks; ++i)
+    if (dst[i]) *dst[i] = data[i];
+}
+
+// Sequences whose new rows one writer workgroup copies.
+template <typename T, int D, int W>
+constexpr int writer_seqs() {
+  return kWriterChunks * 64 * W / (2 * D * (int)sizeof(T) / 16);
+}
+
+// kStore: this workgroup also stores the new rows when it owns the last
+// token (the grid launch); the listed launch leaves that to its writers.
+template <typename T, int D, int B, int W, bool kStore>
 __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
                                            int b, int part) {
   int ctx = p.context_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
   // With a fused append the item that owns the last token (partition 0 for
-  // an empty context) also stores the new rows; no other item of the launch
+  // an empty context) reads it from the new rows; no item of the launch
   // reads that slot.
   const int n_parts = (ctx + p.partition_size - 1) / p.partition_size;
   const bool append = p.new_key != nullptr && part == (n_parts > 0 ? n_parts - 1 : 0);
-  if (append) store_new_token<T, D, B, W>(p, b, h);
+  if (kStore && append) store_new_token<T, D, B, W>(p, b, h);
   if (ctx == 0) {
     if (part == 0) {
       T *out_row = reinterpret_cast<T *>(p.out) + ((size_t)b * p.num_heads + h) * D;
@@ -475,18 +529,27 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
 template <typename T, int D, int B, int W>
 __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
   __shared__ ItemShared<T, D, W> sh;
-  decode_one<T, D, B, W>(p, sh, blockIdx.x, blockIdx.y, p.num_partitions - 1 - (int)blockIdx.z);
+  decode_one<T, D, B, W, true>(p, sh, blockIdx.x, blockIdx.y,
+                               p.num_partitions - 1 - (int)blockIdx.z);
 }
 
 // Workgroups own (head, listed item): the host listed the non-empty
 // (sequence, partition) items, longest first, so no workgroup is empty and
-// the smallest items trail the launch.
+// the smallest items trail the launch.  With a fused append, the rows past
+// the list are writers (write_new_rows), which fill the launch's tail.
 template <typename T, int D, int B, int W>
 __global__ void __launch_bounds__(64 * W) decode_listed_kernel(const DecodeParams p,
                                                                 const WorkList items) {
   __shared__ ItemShared<T, D, W> sh;
-  const uint32_t it = items.item[blockIdx.y];
-  decode_one<T, D, B, W>(p, sh, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu));
+  const int y = blockIdx.y;
+  if (y >= items.count) {
+    constexpr int S = writer_seqs<T, D, W>();
+    const int first = (y - items.count) * S;
+    write_new_rows<T, D, B, W>(p, blockIdx.x, first, min(S, p.num_seqs - first));
+    return;
+  }
+  const uint32_t it = items.item[y];
+  decode_one<T, D, B, W, false>(p, sh, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu));
 }
 
 // Second pass, rows with several partitions only: out = sum_p w_p o_p /
@@ -540,15 +603,17 @@ struct Lists {
 
 template <typename T, int D, int B, int W>
 void launch_listed(const DecodeParams &p, Lists l, hipStream_t stream) {
+  constexpr int S = writer_seqs<T, D, W>();
+  const int writers = p.new_key != nullptr ? (p.num_seqs + S - 1) / S : 0;
   decode_listed_kernel<T, D, B, W>
-      <<<dim3(p.num_heads, l.items->count), 64 * W, 0, stream>>>(p, *l.items);
+      <<<dim3(p.num_heads, l.items->count + writers), 64 * W, 0, stream>>>(p, *l.items);
 }
 
 template <typename T, int D, int B>
 hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_t stream) {
   constexpr int W = kDecodeWaves;
   if (l.items) {
-    if (l.items->count > 0) {
+    if (l.items->count > 0 || (p.new_key != nullptr && num_seqs > 0)) {
       if (l.waves == 2) launch_listed<T, D, B, 2>(p, l, stream);
       else if (l.waves == 4) launch_listed<T, D, B, 4>(p, l, stream);
       else launch_listed<T, D, B, 8>(p, l, stream);

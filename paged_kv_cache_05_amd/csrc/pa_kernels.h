@@ -16,6 +16,7 @@ struct DecodeParams {
   const void *v_pool;
   const int32_t *block_tables;
   const int32_t *context_lens;
+  int num_seqs;
   int num_heads;
   int num_blocks;
   int max_blocks_per_seq;
