@@ -136,7 +136,7 @@ int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int
  *                  workgroup per (head, sequence, partition) is launched
  *                  and empty ones leave at once).  When the mean item is
  *                  shorter than 192 tokens, those workgroups have 4 waves
- *                  (2 at block size 8) instead of 8; the result then
+ *                  instead of 8; the result then
  *                  differs from the unplanned launch's by fp32 rounding
  *                  order, otherwise it is the same bit for bit.  Each entry must be at
  *                  least the device value it copies (equal for the best

@@ -112,12 +112,11 @@ int clamp_ctx(int32_t c, int max_context_len) {
 // late; the rest keep (sequence, partition) order, which keeps neighbouring
 // sequences (for instance parallel samples sharing prompt blocks) close in
 // time and mixes sizes so that concurrently running workgroups stay busy.
-// Waves per workgroup: 8, or, when the mean item is shorter than 12
-// 16-token tiles (8 waves would leave most of them one tile or none), 4
-// (2 at block size 8, whose tiles span two blocks).  Measured on 256
-// sequences of 20..200 tokens: 4 waves 8% / 6% faster than 8 at B = 16 / 64,
-// 2 waves 27% faster at B = 8; 8 waves best on the lognormal batch (median
-// 300 tokens).
+// Waves per workgroup: 8, or 4 when the mean item is shorter than 12
+// 16-token tiles (8 waves would leave most of them one tile or none).
+// Measured on 256 sequences of 20..200 tokens (fused step): 4 waves 12-23%
+// faster than 8 at B = 8 / 16 / 64, and 2-6% faster than 2 waves; 8 waves
+// best on the lognormal batch (median 300 tokens).
 // False when either list would exceed the kernel-argument capacity.
 bool plan_work(const int32_t *host_ctx, int num_seqs, int max_context_len, int part,
                int block_size, pa::WorkList *items, pa::WorkList *merge_rows, int *waves) {
@@ -150,7 +149,7 @@ bool plan_work(const int32_t *host_ctx, int num_seqs, int max_context_len, int p
   items->count = n;
   for (int i = 0; i < n; ++i) items->item[i] = e[i].item;
   constexpr long long kShortItemTokens = 12 * 16;
-  *waves = (long long)n * kShortItemTokens > tokens ? (block_size == 8 ? 2 : 4) : 8;
+  *waves = (long long)n * kShortItemTokens > tokens ? 4 : 8;
   return true;
 }
 

@@ -592,7 +592,7 @@ __global__ void __launch_bounds__(D) merge_listed_kernel(const DecodeParams p,
 }
 
 // Waves per workgroup of the grid launch: 8 (4 and 16 measured slower on
-// the lognormal batch).  The listed launch also has 2- and 4-wave forms for
+// the lognormal batch).  The listed launch also has a 4-wave form for
 // batches of short rows, where 8 waves leave most of them one tile or none.
 constexpr int kDecodeWaves = 8;
 
@@ -614,8 +614,7 @@ hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_
   constexpr int W = kDecodeWaves;
   if (l.items) {
     if (l.items->count > 0 || (p.new_key != nullptr && num_seqs > 0)) {
-      if (l.waves == 2) launch_listed<T, D, B, 2>(p, l, stream);
-      else if (l.waves == 4) launch_listed<T, D, B, 4>(p, l, stream);
+      if (l.waves == 4) launch_listed<T, D, B, 4>(p, l, stream);
       else launch_listed<T, D, B, 8>(p, l, stream);
     }
     if (p.num_partitions > 1 && l.merge_rows && l.merge_rows->count > 0)

@@ -53,7 +53,7 @@ struct WorkList {
 // dtype: 0 = f16, 1 = f32.  `items` (optional) lists the (sequence,
 // partition) work items in launch order, `merge_rows` (optional, needed when
 // items is given and num_partitions > 1) the sequences that span several
-// partitions; `waves` (2, 4 or 8) is the listed launch's waves per
+// partitions; `waves` (4 or 8) is the listed launch's waves per
 // workgroup (the grid launch uses 8).  Returns the launch status.
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
                          int dtype, const WorkList *items, const WorkList *merge_rows,

@@ -328,10 +328,10 @@ def test_write_skips_slots_outside_pool(pa, oracle_lib, device):
 
 
 def planned_waves(ctx, part, block_size):
-    """The planner's waves per workgroup: 4 (2 at B = 8) when the mean
-    (sequence, partition) item is shorter than 12 tiles of 16 tokens."""
+    """The planner's waves per workgroup: 4 when the mean (sequence,
+    partition) item is shorter than 12 tiles of 16 tokens, else 8."""
     items = sum(1 if c == 0 else -(-int(c) // part) for c in ctx)
-    return 8 if items * 12 * 16 <= int(np.sum(ctx)) else (2 if block_size == 8 else 4)
+    return 8 if items * 12 * 16 <= int(np.sum(ctx)) else 4
 
 
 @pytest.mark.parametrize("config,kw,part", [
@@ -359,13 +359,13 @@ def test_host_planned_launch(pa, oracle_lib, device, config, kw, part):
 @pytest.mark.parametrize("B", [8, 16, 32, 64])
 def test_short_rows_use_fewer_waves(pa, oracle_lib, device, B):
     """Batches of short rows (mean item under 192 tokens) run the planned
-    launch with 4 waves per workgroup (2 at B = 8): oracle parity at every
+    launch with 4 waves per workgroup: oracle parity at every
     block size, fp16 and fp32, including one-token rows and ragged tails."""
     for dtype in (W.F16, W.F32):
         ctx = np.random.default_rng(40 + B).integers(1, 180, size=96)
         ctx[:3] = (1, 2, 17)
         wl = W._simple(f"short-rows-b{B}", 40 + B, dtype, 8, 128 if dtype == W.F16 else 64, B, ctx)
-        assert planned_waves(ctx, 4096, B) in (2, 4)
+        assert planned_waves(ctx, 4096, B) == 4
         announce(f"{wl.name} {dtype}: planned short-row launch")
         got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
                          host_ctx=wl.context_lens)
@@ -515,6 +515,20 @@ def test_decode_append_full_last_tile(pa, device, part, host):
     announce(f"decode_append full last tile part={part} host={host}")
     (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, part, host, ctx=ctx,
                                                  slots=slots)
+    assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    assert np.array_equal(fo, so)
+
+
+@pytest.mark.parametrize("config,kw", [(2, {"num_seqs": 100}), (3, {"num_seqs": 70})],
+                         ids=["cfg2-100seqs", "cfg3-70seqs"])
+def test_decode_append_partial_writer_row(pa, device, config, kw):
+    """Batches that do not fill the last writer workgroup of the listed
+    launch (100 sequences at 8 waves: 64 + 36; 70 short rows at 4 waves:
+    32 + 32 + 6): every new row is still stored, bit for bit as the write
+    followed by the decode, and so are the outputs."""
+    wl = workload(config, **kw)
+    announce(f"decode_append partial writer row {wl.name} N={wl.num_seqs}")
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=True)
     assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
     assert np.array_equal(fo, so)
 
