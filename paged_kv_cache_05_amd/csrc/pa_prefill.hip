@@ -447,15 +447,24 @@ prefill_split_kernel(const PrefillParams p, const SplitList items) {
                      (int)((part >> 4) & 15u), (int)(part & 15u) + 1, (int)(part >> 8));
 }
 
-// Merge of a split tile's chunks: grid (heads, split tiles), two threads per
-// query row, each over half the head dims.  The chunks' softmax states
-// combine by the usual rescaling: with M the largest running max,
+// Merge of a split tile's chunks: grid (heads, split tiles, row groups),
+// 256 threads.  D / 4 lanes cover one query row with 16-byte loads, so a
+// wave reads whole rows per instruction and each workgroup takes 256 / (D /
+// 4) rows.  Every chunk's state and partial row are loaded before any
+// arithmetic (one memory round trip per workgroup), then combined by the
+// usual rescaling: with M the largest running max,
 //   out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
 // Rows and invalid sequences follow the unsplit epilogue.
+constexpr int kMergeThreads = 256;
 template <int D>
-__global__ void __launch_bounds__(2 * kQTile) prefill_merge_kernel(const PrefillParams p,
-                                                                   const SplitList merges) {
-  constexpr int kSeg = D / 2;
+constexpr int merge_rows() {
+  return kMergeThreads / (D / 4);
+}
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(const PrefillParams p,
+                                                                       const SplitList merges) {
+  constexpr int kLanesPerRow = D / 4;
+  static_assert(kQTile % merge_rows<D>() == 0, "row groups");
   const int h = blockIdx.x;
   const uint32_t it = merges.item[blockIdx.y], part = merges.part[blockIdx.y];
   const int b = (int)(it >> 16), qt = (int)(it & 0xffffu);
@@ -464,40 +473,45 @@ __global__ void __launch_bounds__(2 * kQTile) prefill_merge_kernel(const Prefill
   const int m = p.query_start[b + 1] - q0;
   const int n = min(max(p.context_lens[b], 0), p.max_context_len);
   const bool bad_seq = m < 0 || m > n || q0 < 0 || q0 + m > p.num_query_rows;
-  const int row = threadIdx.x >> 1, d0 = (threadIdx.x & 1) * kSeg;
+  const int d = (threadIdx.x % kLanesPerRow) * 4;
+  const int row = blockIdx.z * merge_rows<D>() + threadIdx.x / kLanesPerRow;
   const int r = qt * kQTile + row;
   if (r >= m || q0 + r >= p.num_query_rows || q0 + r < 0) return;
+  float2 ml[kMaxChunks];
+  float4 v[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    if (i < nc) {
+      const size_t prow = ((size_t)(slot0 + i) * p.num_heads + h) * kQTile + row;
+      ml[i] = p.part_ml[prow];
+      v[i] = *reinterpret_cast<const float4 *>(p.part_o + prow * D + d);
+    }
+  }
   float M = -INFINITY;
-  for (int i = 0; i < nc; ++i)
-    M = fmaxf(M, p.part_ml[((size_t)(slot0 + i) * p.num_heads + h) * kQTile + row].x);
-  float L = 0.f, acc[kSeg];
 #pragma unroll
-  for (int e = 0; e < kSeg; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nc; ++i) {
-    const size_t prow = ((size_t)(slot0 + i) * p.num_heads + h) * kQTile + row;
-    const float2 ml = p.part_ml[prow];
-    const float wgt = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    L += wgt * ml.y;
-    const float4 *po = reinterpret_cast<const float4 *>(p.part_o + prow * D + d0);
+  for (int i = 0; i < kMaxChunks; ++i)
+    if (i < nc) M = fmaxf(M, ml[i].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int e = 0; e < kSeg / 4; ++e) {
-      const float4 v = po[e];
-      acc[4 * e] += wgt * v.x;
-      acc[4 * e + 1] += wgt * v.y;
-      acc[4 * e + 2] += wgt * v.z;
-      acc[4 * e + 3] += wgt * v.w;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    if (i < nc) {
+      const float wgt = ml[i].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[i].x - M);
+      L += wgt * ml[i].y;
+      acc.x += wgt * v[i].x;
+      acc.y += wgt * v[i].y;
+      acc.z += wgt * v[i].z;
+      acc.w += wgt * v[i].w;
     }
   }
   const float inv = (bad_seq || !(L > 0.f)) ? NAN : 1.f / L;
-  _Float16 *orow =
-      static_cast<_Float16 *>(p.out) + ((int64_t)(q0 + r) * p.num_heads + h) * D + d0;
-#pragma unroll
-  for (int e = 0; e < kSeg / 4; ++e) {
-    half4 o4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o4[k] = (_Float16)(acc[4 * e + k] * inv);
-    *reinterpret_cast<half4 *>(orow + 4 * e) = o4;
-  }
+  half4 o4;
+  o4[0] = (_Float16)(acc.x * inv);
+  o4[1] = (_Float16)(acc.y * inv);
+  o4[2] = (_Float16)(acc.z * inv);
+  o4[3] = (_Float16)(acc.w * inv);
+  *reinterpret_cast<half4 *>(static_cast<_Float16 *>(p.out) +
+                             ((int64_t)(q0 + r) * p.num_heads + h) * D + d) = o4;
 }
 
 template <int D, int B>
@@ -509,8 +523,8 @@ hipError_t launch_db(const PrefillParams &p, int num_seqs, int max_query_len,
       prefill_split_kernel<D, B>
           <<<dim3(p.num_heads, split->count), kThreads, 0, stream>>>(p, *split);
     if (merges && merges->count > 0)
-      prefill_merge_kernel<D>
-          <<<dim3(p.num_heads, merges->count), 2 * kQTile, 0, stream>>>(p, *merges);
+      prefill_merge_kernel<D><<<dim3(p.num_heads, merges->count, kQTile / merge_rows<D>()),
+                                kMergeThreads, 0, stream>>>(p, *merges);
     return hipGetLastError();
   }
   if (items) {
