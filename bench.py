@@ -32,6 +32,7 @@ prompt mix and on shared-prefix requests and prints its own line.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -53,10 +54,16 @@ PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_05_amd", "csrc", f)
 
 
 def kernel_digest(sources=None):
+    """Digest of the kernel sources' code: comments and whitespace are
+    dropped first, so an edit of a comment keeps stored counters valid and
+    any change to the code invalidates them."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES if sources is None else sources:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -214,7 +214,7 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   const unsigned num_blocks = (unsigned)p.num_blocks;
   bool bad = false;
   // Fused append: the token at position ctx - 1 comes from the new rows,
-  // not from the pool (which this workgroup is writing it to).
+  // not from the pool, which the same launch is writing it to.
   const int last = ctx - 1;
   const char *nk = append ? reinterpret_cast<const char *>(p.new_key) + row * D * sizeof(T)
                           : nullptr;
@@ -424,11 +424,9 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   if (threadIdx.x == 0) p.part_ml[row * NP + part] = make_float2(M, lsum);
 }
 
-// Workgroup for head h of sequence b, partition `part`: clamps the context
-// from the device array, writes a zero row for an empty context (partition
-// 0 only) and leaves at once when the partition holds no token.
-// Fused append: store the new token's K and V rows of (b, h) at its slot
-// (slots outside the pool are skipped, as pa_write_kv does).
+// Fused append in the grid launch: the workgroup that owns the new token
+// stores its K and V rows of (b, h) at its slot (slots outside the pool are
+// skipped, as pa_write_kv does).
 template <typename T, int D, int B, int W>
 __device__ __forceinline__ void store_new_token(const DecodeParams &p, int b, int h) {
   const int64_t slot = p.slot_mapping[b];
@@ -496,8 +494,11 @@ constexpr int writer_seqs() {
   return kWriterChunks * 64 * W / (2 * D * (int)sizeof(T) / 16);
 }
 
-// kStore: this workgroup also stores the new rows when it owns the last
-// token (the grid launch); the listed launch leaves that to its writers.
+// Workgroup for head h of sequence b, partition `part`: clamps the context
+// from the device array, writes a zero row for an empty context (partition
+// 0 only) and leaves at once when the partition holds no token.  kStore:
+// it also stores the new rows when it owns the last token (the grid
+// launch); the listed launch leaves that to its writers.
 template <typename T, int D, int B, int W, bool kStore>
 __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
                                            int b, int part) {
