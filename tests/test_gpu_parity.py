@@ -533,6 +533,18 @@ def test_decode_append_partial_writer_row(pa, device, config, kw):
     assert np.array_equal(fo, so)
 
 
+def test_decode_append_over_capacity(pa, device):
+    """With more items than one launch can list, the fused step falls back to
+    the grid launch, whose owning workgroups store the new rows: still bit
+    for bit the write followed by the decode."""
+    ctx = np.random.default_rng(19).integers(1, 90, size=1100)
+    wl = W._simple("many-seqs-append", 19, W.F16, 2, 64, 16, ctx)
+    announce("decode_append over list capacity")
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, partition_size=32, host=True)
+    assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
+    assert np.array_equal(fo, so)
+
+
 def test_decode_append_empty_context_still_writes(pa, device):
     """A sequence with context 0 gets a zero row and its new token is still
     stored (as pa_write_kv would)."""
