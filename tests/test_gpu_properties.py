@@ -43,9 +43,11 @@ def test_random_shapes_match_oracle(pa, oracle_lib, device, case):
     assert np.all(got[ctx_dev == 0] == 0)
 
 
-def test_step_replayed_from_a_hip_graph(pa, oracle_lib, device):
-    """copy_blocks + write_kv + decode captured once and replayed three times,
-    with eager work and synchronisation between replays; every replay
+@pytest.mark.parametrize("fused", [False, True], ids=["write-then-decode", "decode-append"])
+def test_step_replayed_from_a_hip_graph(pa, oracle_lib, device, fused):
+    """copy_blocks + write_kv + decode (or the fused decode_append, whose
+    listed launch has writer workgroups) captured once and replayed three
+    times, with eager work and synchronisation between replays; every replay
     reproduces the eager result bit for bit."""
     wl = W.config1()
     k0, v0 = dev(wl.k_pool_pre, device), dev(wl.v_pool_pre, device)
@@ -59,6 +61,11 @@ def test_step_replayed_from_a_hip_graph(pa, oracle_lib, device):
 
     def step():
         pa.pa_copy_blocks(k, v, pairs)
+        if fused:
+            pa.pa_decode_append(out, q, key, val, k, v, tables, ctx, slots, float(wl.scale),
+                                wl.max_context_len, partition_size=16, workspace=ws,
+                                host_context_lens=wl.context_lens)
+            return
         pa.pa_write_kv(key, val, k, v, slots)
         pa.pa_decode(out, q, k, v, tables, ctx, float(wl.scale), wl.max_context_len,
                      partition_size=16, workspace=ws, host_context_lens=wl.context_lens)
