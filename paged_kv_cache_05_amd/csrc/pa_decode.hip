@@ -49,8 +49,9 @@ namespace pa {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-// An int32 in the constant address space (read-only for the kernel's life).
+// Integers in the constant address space (read-only for the kernel's life).
 typedef const __attribute__((address_space(4))) int32_t ConstI32;
+typedef const __attribute__((address_space(4))) int64_t ConstI64;
 
 // 16-byte chunks each writer thread of a fused append copies (its loads are
 // issued together, then its stores).
@@ -424,25 +425,41 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   if (threadIdx.x == 0) p.part_ml[row * NP + part] = make_float2(M, lsum);
 }
 
-// Fused append in the grid launch: the workgroup that owns the new token
-// stores its K and V rows of (b, h) at its slot (slots outside the pool are
-// skipped, as pa_write_kv does).
+// Fused append in the grid launch: the extra column of workgroups (head
+// index num_heads) copies sequence b's new K and V rows of every head to the
+// token's slot (a slot outside the pool is skipped, as pa_write_kv does).
+// No workgroup of the launch reads that slot: the attention takes the new
+// token from its input rows.  Each pass loads its chunks, then stores them.
 template <typename T, int D, int B, int W>
-__device__ __forceinline__ void store_new_token(const DecodeParams &p, int b, int h) {
-  const int64_t slot = p.slot_mapping[b];
+__device__ __forceinline__ void write_seq_rows(const DecodeParams &p, int b) {
+  constexpr int kC = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  constexpr int kThreads = 64 * W;
+  const int64_t slot = ((const ConstI64 *)p.slot_mapping)[b];
   if (slot < 0 || slot >= (int64_t)p.num_blocks * B) return;
-  constexpr int kC = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
-  const int64_t blk = slot / B;
-  const int off = (int)(slot - blk * B);
-  const size_t src = ((size_t)b * p.num_heads + h) * kC;
-  const size_t dst = (((size_t)blk * p.num_heads + h) * B + off) * kC;
-  for (int c = threadIdx.x; c < 2 * kC; c += 64 * W) {
-    if (c < kC)
-      reinterpret_cast<uint4 *>(const_cast<void *>(p.k_pool))[dst + c] =
-          reinterpret_cast<const uint4 *>(p.new_key)[src + c];
-    else
-      reinterpret_cast<uint4 *>(const_cast<void *>(p.v_pool))[dst + c - kC] =
-          reinterpret_cast<const uint4 *>(p.new_value)[src + c - kC];
+  const size_t blk = (size_t)(slot / B), off = (size_t)(slot % B);
+  const int total = 2 * p.num_heads * kC;
+  for (int base = 0; base < total; base += kThreads * kWriterChunks) {
+    uint4 data[kWriterChunks];
+    uint4 *dst[kWriterChunks];
+#pragma unroll
+    for (int i = 0; i < kWriterChunks; ++i) {
+      const int c = base + (int)threadIdx.x + i * kThreads;
+      dst[i] = nullptr;
+      data[i] = make_uint4(0, 0, 0, 0);
+      if (c < total) {
+        const int h = c / (2 * kC);
+        const int e = c % (2 * kC);
+        const bool is_k = e < kC;
+        const int ch = is_k ? e : e - kC;
+        const size_t src = ((size_t)b * p.num_heads + h) * kC + ch;
+        const size_t at = ((blk * p.num_heads + h) * B + off) * kC + ch;
+        data[i] = reinterpret_cast<const uint4 *>(is_k ? p.new_key : p.new_value)[src];
+        dst[i] = reinterpret_cast<uint4 *>(const_cast<void *>(is_k ? p.k_pool : p.v_pool)) + at;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWriterChunks; ++i)
+      if (dst[i]) *dst[i] = data[i];
   }
 }
 
@@ -496,10 +513,9 @@ constexpr int writer_seqs() {
 
 // Workgroup for head h of sequence b, partition `part`: clamps the context
 // from the device array, writes a zero row for an empty context (partition
-// 0 only) and leaves at once when the partition holds no token.  kStore:
-// it also stores the new rows when it owns the last token (the grid
-// launch); the listed launch leaves that to its writers.
-template <typename T, int D, int B, int W, bool kStore>
+// 0 only) and leaves at once when the partition holds no token.  With a
+// fused append the launch's writer workgroups store the new rows.
+template <typename T, int D, int B, int W>
 __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
                                            int b, int part) {
   int ctx = p.context_lens[b];
@@ -509,7 +525,6 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
   // reads that slot.
   const int n_parts = (ctx + p.partition_size - 1) / p.partition_size;
   const bool append = p.new_key != nullptr && part == (n_parts > 0 ? n_parts - 1 : 0);
-  if (kStore && append) store_new_token<T, D, B, W>(p, b, h);
   if (ctx == 0) {
     if (part == 0) {
       T *out_row = reinterpret_cast<T *>(p.out) + ((size_t)b * p.num_heads + h) * D;
@@ -526,12 +541,17 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
 // the slowest grid dimension, counted down: the last partitions, which
 // exist only for the longest sequences, are dispatched first and partition
 // 0 (every row, including the short ones) last, so the work that trails
-// the launch is the smallest.
+// the launch is the smallest.  With a fused append the grid has one more
+// head column: its workgroups in the last-dispatched slice are the writers
+// (write_seq_rows), one per sequence; the others leave at once.
 template <typename T, int D, int B, int W>
 __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
   __shared__ ItemShared<T, D, W> sh;
-  decode_one<T, D, B, W, true>(p, sh, blockIdx.x, blockIdx.y,
-                               p.num_partitions - 1 - (int)blockIdx.z);
+  if ((int)blockIdx.x == p.num_heads) {
+    if (blockIdx.z == gridDim.z - 1) write_seq_rows<T, D, B, W>(p, blockIdx.y);
+    return;
+  }
+  decode_one<T, D, B, W>(p, sh, blockIdx.x, blockIdx.y, p.num_partitions - 1 - (int)blockIdx.z);
 }
 
 // Workgroups own (head, listed item): the host listed the non-empty
@@ -550,7 +570,7 @@ __global__ void __launch_bounds__(64 * W) decode_listed_kernel(const DecodeParam
     return;
   }
   const uint32_t it = items.item[y];
-  decode_one<T, D, B, W, false>(p, sh, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu));
+  decode_one<T, D, B, W>(p, sh, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu));
 }
 
 // Second pass, rows with several partitions only: out = sum_p w_p o_p /
@@ -623,8 +643,9 @@ hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_
           <<<dim3(p.num_heads, l.merge_rows->count), D, 0, stream>>>(p, *l.merge_rows);
     return hipGetLastError();
   }
-  decode_kernel<T, D, B, W>
-      <<<dim3(p.num_heads, num_seqs, p.num_partitions), 64 * W, 0, stream>>>(p);
+  decode_kernel<T, D, B, W><<<dim3(p.num_heads + (p.new_key != nullptr ? 1 : 0), num_seqs,
+                                   p.num_partitions),
+                              64 * W, 0, stream>>>(p);
   if (p.num_partitions > 1)
     merge_kernel<T, D><<<dim3(p.num_heads, num_seqs), D, 0, stream>>>(p);
   return hipGetLastError();

@@ -545,14 +545,15 @@ def test_decode_append_over_capacity(pa, device):
     assert np.array_equal(fo, so)
 
 
-def test_decode_append_empty_context_still_writes(pa, device):
+@pytest.mark.parametrize("host", [True, False], ids=["listed", "grid"])
+def test_decode_append_empty_context_still_writes(pa, device, host):
     """A sequence with context 0 gets a zero row and its new token is still
-    stored (as pa_write_kv would)."""
-    announce("decode_append empty context")
+    stored (as pa_write_kv would), in either launch form."""
+    announce(f"decode_append empty context host={host}")
     wl = workload(1)
     ctx = wl.context_lens.copy()
     ctx[0] = 0
-    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=True, ctx=ctx)
+    (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=host, ctx=ctx)
     assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
     assert np.array_equal(fo, so)
     assert not np.any(fo[0].view(wl.q.dtype))
