@@ -16,9 +16,14 @@
 //    a group of lanes: at fp16/head_dim 128 one row is 256 bytes = 16 lanes,
 //    so one wave load covers 4 consecutive tokens and a 16-token tile is 4
 //    loads of K and 4 of V, each 1 KiB contiguous inside one block.
-//  * The physical block of a tile comes from one scalar load of the block
-//    table entry (block index = token / B, offset = token % B), so address
-//    translation costs one s_load per tile and no vector work.
+//  * The physical block of a tile comes from one load of the block table
+//    entry (block index = token / B, offset = token % B): a scalar load for
+//    tiles fetched while another is in flight (its wait leaves their loads
+//    in flight), a vector load for a wave's first and ragged tiles, which
+//    have nothing else in flight.  Translation costs one load per tile.
+//  * With a fused append the new token is read from its input rows, and
+//    extra writer workgroups in the same launch store those rows at their
+//    slots; no workgroup of the launch reads them there.
 //  * q.k per token: v_dot2 (fp16 pairs into fp32) on the lane's chunk, then a
 //    DPP row reduction over the lanes of the token (quad_perm, half-mirror,
 //    mirror).  Every lane of the row ends up holding the token's score.
