@@ -520,9 +520,9 @@ def main():
     # workloads are the short-request batch (any block size) and the
     # long-context OPT-175B-shaped layer, whose pools (24 GB each) already
     # dwarf the caches, so two of them rotate.
-    wl = {"opt13b": lambda: W.config2(host=False),
-          "short": lambda: W.config3(block_size=args.block_size, host=False),
-          "long": lambda: W.config5(host=False)}[args.config]()
+    wl = {"opt13b": lambda: W.opt13b_layer(host=False),
+          "short": lambda: W.short_rows(block_size=args.block_size, host=False),
+          "long": lambda: W.long_context(host=False)}[args.config]()
     N, H, D, B = wl.num_seqs, wl.num_heads, wl.head_dim, wl.block_size
     L = min(args.layers, 2) if args.config == "long" else args.layers
     default_config = args.config == "opt13b"

@@ -82,12 +82,12 @@ def cached(key):
     return W.make(name, **kw)
 
 
-def workload(config, **kw):
-    return cached((config,) + tuple(sorted(kw.items())))
+def workload(name, **kw):
+    return cached((name,) + tuple(sorted(kw.items())))
 
 
 # ---------------------------------------------------------------------------
-# the five configurations
+# the five workloads
 # ---------------------------------------------------------------------------
 
 def step_on_gpu(pa, wl, device):
@@ -109,14 +109,14 @@ def step_on_oracle(oracle, wl):
     return k, v
 
 
-@pytest.mark.parametrize("config,kw", [
-    (1, {}),
-    (2, {}),
-    (3, {"block_size": 16}),
-    (4, {}),
-], ids=["cfg1-tiny-fp32", "cfg2-opt13b", "cfg3-short", "cfg4-cow"])
-def test_step_then_decode(pa, oracle_lib, device, config, kw):
-    wl = workload(config, **kw)
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("opt13b", {}),
+    ("short", {"block_size": 16}),
+    ("cow", {}),
+], ids=["tiny-fp32", "opt13b", "short", "cow"])
+def test_step_then_decode(pa, oracle_lib, device, name, kw):
+    wl = workload(name, **kw)
     announce(f"{wl.name}: N={wl.num_seqs} H={wl.num_heads} D={wl.head_dim} B={wl.block_size} "
              f"NB={wl.num_blocks} pairs={len(wl.block_mapping)} tokens={len(wl.slot_mapping)}")
     k, v = step_on_gpu(pa, wl, device)
@@ -134,24 +134,24 @@ def test_step_then_decode(pa, oracle_lib, device, config, kw):
 
 @pytest.mark.parametrize("B", [8, 16, 32, 64])
 def test_block_size_sweep(pa, oracle_lib, device, B):
-    """Config 3's sweep: same sequences and logical K/V for B = 8..64; every B
+    """The short-row sweep: same sequences and logical K/V for B = 8..64; every B
     matches the oracle and the GPU output is bit-identical across B (the
     kernel's summation order depends on logical positions only)."""
-    wl = workload(3, block_size=B)
+    wl = workload("short", block_size=B)
     announce(f"{wl.name}: N={wl.num_seqs} B={B}")
     got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
     assert_close(got, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
-    base = workload(3, block_size=16)
+    base = workload("short", block_size=16)
     if B != 16:
         ref = gpu_decode(pa, base, dev(base.k_pool, device), dev(base.v_pool, device), device)
         assert np.array_equal(bits(got), bits(ref))
 
 
-def test_config5_long_context_sampled(pa, oracle_lib, device):
+def test_long_context_sampled(pa, oracle_lib, device):
     """OPT-175B layer shape, all 96 heads, contexts 4K-16K: the full batch on the
     GPU (device-filled pools), checked against the oracle on sampled rows with
     the real block table."""
-    wl = W.config5(host=False)
+    wl = W.long_context(host=False)
     announce(f"{wl.name}: N={wl.num_seqs} H={wl.num_heads} NB={wl.num_blocks} filling pools")
     k, v = W.device_pools(wl, device)
     announce(f"{wl.name}: pa_decode default partition")
@@ -184,7 +184,7 @@ def test_config5_long_context_sampled(pa, oracle_lib, device):
 
 @pytest.mark.parametrize("part", [16, 48, 128, 256, 512, 1024, 4096])
 def test_partition_sizes(pa, oracle_lib, device, part):
-    wl = workload(2, num_seqs=24, num_heads=8)
+    wl = workload("opt13b", num_seqs=24, num_heads=8)
     announce(f"{wl.name} small: partition {part}")
     got = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device,
                      partition_size=part)
@@ -192,7 +192,7 @@ def test_partition_sizes(pa, oracle_lib, device, part):
 
 
 def test_placement_invariance_bit_identical(pa, device):
-    wl = workload(2, num_seqs=24, num_heads=8)
+    wl = workload("opt13b", num_seqs=24, num_heads=8)
     ref = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
     for s in range(2):
         r = W.relayout(wl, s)
@@ -202,7 +202,7 @@ def test_placement_invariance_bit_identical(pa, device):
 
 
 def test_shared_prefix_bit_identical_to_private_copies(pa, device):
-    wl = workload(4, num_prompts=6, samples=6, num_heads=4)
+    wl = workload("cow", num_prompts=6, samples=6, num_heads=4)
     ref = gpu_decode(pa, wl, dev(wl.k_pool, device), dev(wl.v_pool, device), device)
     r = W.relayout(wl, 9)
     got = gpu_decode(pa, r, dev(r.k_pool, device), dev(r.v_pool, device), device)
@@ -242,7 +242,7 @@ def test_zero_context_and_max_context(pa, oracle_lib, device):
 
 
 def test_out_of_range_table_entry_poisons_only_its_row(pa, oracle_lib, device):
-    wl = workload(2, num_seqs=24, num_heads=8)
+    wl = workload("opt13b", num_seqs=24, num_heads=8)
     tables = wl.block_tables.copy()
     victim = int(np.argmax(wl.context_lens))
     tables[victim, 1] = wl.num_blocks + 1000  # outside the pool: the kernel must not read it
@@ -258,8 +258,8 @@ def test_out_of_range_table_entry_poisons_only_its_row(pa, oracle_lib, device):
 def test_workspace_contents_ignored_and_reused(pa, oracle_lib, device):
     """Workspace contents on entry do not matter: one buffer, filled with NaN
     bit patterns between calls, serves calls of different batch shapes."""
-    big = workload(2, num_seqs=24, num_heads=8)
-    small = workload(3, block_size=16, num_seqs=12, num_heads=4)
+    big = workload("opt13b", num_seqs=24, num_heads=8)
+    small = workload("short", block_size=16, num_seqs=12, num_heads=4)
     n = pa.pa_decode_workspace_bytes(big.num_seqs, big.num_heads, 128, big.max_context_len, 32)
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     kb, vb = dev(big.k_pool, device), dev(big.v_pool, device)
@@ -334,19 +334,19 @@ def planned_waves(ctx, part, block_size):
     return 8 if items * 12 * 16 <= int(np.sum(ctx)) else 4
 
 
-@pytest.mark.parametrize("config,kw,part", [
-    (1, {}, 16), (1, {}, 0), (2, {}, 0), (2, {}, 256), (2, {}, 1024), (3, {"block_size": 8}, 0),
-    (3, {"block_size": 32}, 64), (4, {}, 0), (4, {}, 128),
-    (2, {"num_seqs": 24, "num_heads": 8}, 48), (2, {"num_seqs": 3, "num_heads": 2}, 0),
-], ids=["cfg1-p16", "cfg1-auto", "cfg2-auto", "cfg2-p256", "cfg2-p1024", "cfg3-b8-auto",
-        "cfg3-b32-p64", "cfg4-auto", "cfg4-p128", "cfg2small-p48", "cfg2tiny-auto"])
-def test_host_planned_launch(pa, oracle_lib, device, config, kw, part):
+@pytest.mark.parametrize("name,kw,part", [
+    ("tiny", {}, 16), ("tiny", {}, 0), ("opt13b", {}, 0), ("opt13b", {}, 256), ("opt13b", {}, 1024), ("short", {"block_size": 8}, 0),
+    ("short", {"block_size": 32}, 64), ("cow", {}, 0), ("cow", {}, 128),
+    ("opt13b", {"num_seqs": 24, "num_heads": 8}, 48), ("opt13b", {"num_seqs": 3, "num_heads": 2}, 0),
+], ids=["tiny-p16", "tiny-auto", "opt13b-auto", "opt13b-p256", "opt13b-p1024", "short-b8-auto",
+        "short-b32-p64", "cow-auto", "cow-p128", "opt13b-small-p48", "opt13b-tiny-auto"])
+def test_host_planned_launch(pa, oracle_lib, device, name, kw, part):
     """With host-side context lengths the library launches only the non-empty
     (sequence, partition) items, long ones first.  With an explicit partition
     size and 8-wave workgroups the results are bit-identical to the unplanned
     launch (same per-partition reduction order); with partition_size 0 the
     library also picks the partition size from the lengths."""
-    wl = workload(config, **kw)
+    wl = workload(name, **kw)
     k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
     announce(f"{wl.name}: planned vs unplanned, partition {part}")
     plain = gpu_decode(pa, wl, k, v, device, partition_size=part)
@@ -375,7 +375,7 @@ def test_short_rows_use_fewer_waves(pa, oracle_lib, device, B):
 def test_host_lengths_as_upper_bound(pa, oracle_lib, device):
     """Host lengths may exceed the device ones (the extra items find nothing
     to do); empty sequences still get zero rows."""
-    wl = workload(2, num_seqs=24, num_heads=8)
+    wl = workload("opt13b", num_seqs=24, num_heads=8)
     ctx = wl.context_lens.copy()
     ctx[[3, 7]] = 0
     host = np.minimum(ctx + np.random.default_rng(2).integers(0, 300, size=len(ctx)),
@@ -399,7 +399,7 @@ def test_host_plan_over_capacity_falls_back(pa, oracle_lib, device):
 
 
 def test_nondefault_stream(pa, oracle_lib, device):
-    wl = workload(1)
+    wl = workload("tiny")
     s = torch.cuda.Stream()
     k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
     q = dev(wl.q, device)
@@ -424,7 +424,7 @@ def test_pending_runtime_error_is_not_taken_for_the_launch(pa, oracle_lib, devic
     assert len(runtimes) == 1
     hip = ctypes.CDLL(runtimes[0])
     hip.hipGetDevice.argtypes = [ctypes.c_void_p]
-    wl = workload(1)
+    wl = workload("tiny")
     k, v = dev(wl.k_pool_pre, device), dev(wl.v_pool_pre, device)
     key, val = dev(wl.new_key, device), dev(wl.new_value, device)
     slots = dev(wl.slot_mapping, device)
@@ -479,15 +479,15 @@ def fused_and_split(pa, wl, device, partition_size=0, host=False, ctx=None, slot
     return res
 
 
-@pytest.mark.parametrize("config,kw", [(1, {}), (2, {}), (3, {"block_size": 8}),
-                                       (3, {"block_size": 64})],
-                         ids=["cfg1", "cfg2", "cfg3-b8", "cfg3-b64"])
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("opt13b", {}), ("short", {"block_size": 8}),
+                                       ("short", {"block_size": 64})],
+                         ids=["tiny", "opt13b", "short-b8", "short-b64"])
 @pytest.mark.parametrize("part,host", [(0, False), (0, True), (64, False), (64, True), (16, True)])
-def test_decode_append_equals_write_then_decode(pa, oracle_lib, device, config, kw, part, host):
+def test_decode_append_equals_write_then_decode(pa, oracle_lib, device, name, kw, part, host):
     """The fused step gives the same pools and the same outputs, bit for
     bit, as the write followed by the decode -- with the new token in a
     split partition (64, 16) and in either launch form."""
-    wl = workload(config, **kw)
+    wl = workload(name, **kw)
     announce(f"decode_append {wl.name} part={part} host={host}")
     (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, part, host)
     assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
@@ -504,7 +504,7 @@ def test_decode_append_full_last_tile(pa, device, part, host):
     """Contexts that end exactly on a 16-token tile: the tile holding the new
     token is full, and the fused step must still match the write followed by
     the decode bit for bit (pools and outputs)."""
-    wl = workload(2)
+    wl = workload("opt13b")
     ctx = wl.context_lens.copy()
     ctx = np.where(ctx >= 16, ctx // 16 * 16, ctx).astype(ctx.dtype)
     assert np.sum(ctx % 16 == 0) > len(ctx) // 2
@@ -519,14 +519,14 @@ def test_decode_append_full_last_tile(pa, device, part, host):
     assert np.array_equal(fo, so)
 
 
-@pytest.mark.parametrize("config,kw", [(2, {"num_seqs": 100}), (3, {"num_seqs": 70})],
-                         ids=["cfg2-100seqs", "cfg3-70seqs"])
-def test_decode_append_partial_writer_row(pa, device, config, kw):
+@pytest.mark.parametrize("name,kw", [("opt13b", {"num_seqs": 100}), ("short", {"num_seqs": 70})],
+                         ids=["opt13b-100seqs", "short-70seqs"])
+def test_decode_append_partial_writer_row(pa, device, name, kw):
     """Batches that do not fill the last writer workgroup of the listed
     launch (100 sequences at 8 waves: 64 + 36; 70 short rows at 4 waves:
     32 + 32 + 6): every new row is still stored, bit for bit as the write
     followed by the decode, and so are the outputs."""
-    wl = workload(config, **kw)
+    wl = workload(name, **kw)
     announce(f"decode_append partial writer row {wl.name} N={wl.num_seqs}")
     (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=True)
     assert np.array_equal(fk, sk) and np.array_equal(fv, sv)
@@ -550,7 +550,7 @@ def test_decode_append_empty_context_still_writes(pa, device, host):
     """A sequence with context 0 gets a zero row and its new token is still
     stored (as pa_write_kv would), in either launch form."""
     announce(f"decode_append empty context host={host}")
-    wl = workload(1)
+    wl = workload("tiny")
     ctx = wl.context_lens.copy()
     ctx[0] = 0
     (fk, fv), fo, (sk, sv), so = fused_and_split(pa, wl, device, host=host, ctx=ctx)
@@ -563,7 +563,7 @@ def test_decode_append_skips_slots_outside_pool(pa, device):
     """A slot outside the pool is not written; the attention still uses the
     new row for the last position, which equals the normal step's output."""
     announce("decode_append slot outside pool")
-    wl = workload(1)
+    wl = workload("tiny")
     slots = wl.slot_mapping.copy()
     slots[2] = -1
     (fk, fv), fo, _, _ = fused_and_split(pa, wl, device, slots=slots)

@@ -49,7 +49,7 @@ def test_step_replayed_from_a_hip_graph(pa, oracle_lib, device, fused):
     listed launch has writer workgroups) captured once and replayed three
     times, with eager work and synchronisation between replays; every replay
     reproduces the eager result bit for bit."""
-    wl = W.config1()
+    wl = W.tiny_fp32()
     k0, v0 = dev(wl.k_pool_pre, device), dev(wl.v_pool_pre, device)
     k, v = k0.clone(), v0.clone()
     pairs, key, val, slots = (dev(wl.block_mapping, device), dev(wl.new_key, device),

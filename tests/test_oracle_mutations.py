@@ -59,16 +59,16 @@ MUTATIONS = {
 # counts as the pin catching it.
 PINS = {
     "half-decoder": lambda o: pins.test_half_decoder_exhaustive(o),
-    "dense-cfg1": lambda o: pins.test_dense_attention_after_gather(o, lambda: W.config1()),
-    "dense-cfg3-b8": lambda o: pins.test_dense_attention_after_gather(
-        o, lambda: W.config3(block_size=8, num_seqs=8, num_heads=2)),
+    "dense-tiny": lambda o: pins.test_dense_attention_after_gather(o, lambda: W.tiny_fp32()),
+    "dense-short-b8": lambda o: pins.test_dense_attention_after_gather(
+        o, lambda: W.short_rows(block_size=8, num_seqs=8, num_heads=2)),
     "decimal": lambda o: [pins.test_decimal_brute_force(o, s) for s in range(6)],
     "one-token": lambda o: pins.test_single_token_returns_v_exactly(o),
     "weights": lambda o: pins.test_weights_sum_to_one(o),
     "two-tokens": lambda o: pins.test_two_tokens_logistic(o),
     "translation": lambda o: [pins.test_translation_matches_append_process(o, B) for B in (4, 16)],
     "cow-example": lambda o: pins.test_cow_worked_example(o),
-    "step-cfg1": lambda o: pins.test_step_reproduces_placement(o, lambda: W.config1()),
+    "step-tiny": lambda o: pins.test_step_reproduces_placement(o, lambda: W.tiny_fp32()),
     "write-read-back": lambda o: pins.test_write_then_read_back(o),
     "sharing-diagram": lambda o: pins.test_sharing_diagram(o),
     "prefill-sdpa": lambda o: [pins.test_prefill_equals_causal_sdpa(o, c) for c in range(3)],

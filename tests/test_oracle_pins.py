@@ -66,12 +66,12 @@ def test_half_decoder_exhaustive(oracle_lib):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("make", [
-    lambda: W.config1(),
-    lambda: W.config2(num_seqs=6, num_heads=3),
-    lambda: W.config3(block_size=8, num_seqs=8, num_heads=2),
-    lambda: W.config3(block_size=64, num_seqs=8, num_heads=2),
-    lambda: W.config4(num_prompts=2, samples=3, num_heads=2),
-], ids=["cfg1", "cfg2-small", "cfg3-b8-small", "cfg3-b64-small", "cfg4-small"])
+    lambda: W.tiny_fp32(),
+    lambda: W.opt13b_layer(num_seqs=6, num_heads=3),
+    lambda: W.short_rows(block_size=8, num_seqs=8, num_heads=2),
+    lambda: W.short_rows(block_size=64, num_seqs=8, num_heads=2),
+    lambda: W.shared_prompts(num_prompts=2, samples=3, num_heads=2),
+], ids=["tiny", "opt13b-small", "short-b8-small", "short-b64-small", "cow-small"])
 def test_dense_attention_after_gather(oracle_lib, make):
     """The block-wise form equals standard attention (zhaifeiyue summary: the
     rewrite is mathematically equivalent because the softmax denominator
@@ -134,14 +134,14 @@ def test_decimal_brute_force(oracle_lib, seed):
 
 
 def test_single_token_returns_v_exactly(oracle_lib):
-    wl = W.config1()
+    wl = W.tiny_fp32()
     out = run_decode(oracle_lib, wl)
     b = int(np.flatnonzero(wl.context_lens == 1)[0])
     assert np.array_equal(out[b], wl.logical_v[b][0].astype(np.float64))
 
 
 def test_weights_sum_to_one(oracle_lib):
-    wl = W.config3(block_size=16, num_seqs=5, num_heads=3)
+    wl = W.short_rows(block_size=16, num_seqs=5, num_heads=3)
     _, w = run_decode(oracle_lib, wl, return_weights=True)
     for b in range(wl.num_seqs):
         n = int(wl.context_lens[b])
@@ -150,7 +150,7 @@ def test_weights_sum_to_one(oracle_lib):
 
 
 def test_zero_query_gives_mean_of_values(oracle_lib):
-    wl = W.config3(block_size=32, num_seqs=4, num_heads=2)
+    wl = W.short_rows(block_size=32, num_seqs=4, num_heads=2)
     wl.q = np.zeros_like(wl.q)
     out = run_decode(oracle_lib, wl)
     for b in range(wl.num_seqs):
@@ -159,7 +159,7 @@ def test_zero_query_gives_mean_of_values(oracle_lib):
 
 
 def test_equal_keys_give_mean_of_values(oracle_lib):
-    wl = W.config1()
+    wl = W.tiny_fp32()
     k = wl.k_pool.copy()
     k[np.isfinite(k)] = 0.75  # every stored key row identical
     out = oracle_lib.decode(wl.q, k, wl.v_pool, wl.block_tables, wl.context_lens, wl.scale)
@@ -189,7 +189,7 @@ def test_two_tokens_logistic(oracle_lib):
 
 
 def test_empty_context_is_zero(oracle_lib):
-    wl = W.config1()
+    wl = W.tiny_fp32()
     ctx = wl.context_lens.copy()
     ctx[2] = 0
     out = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, ctx, wl.scale)
@@ -199,7 +199,7 @@ def test_empty_context_is_zero(oracle_lib):
 def test_unused_slots_never_read(oracle_lib):
     """Slots past the filled count hold NaN in every workload; the oracle
     output is finite, and stays bit-identical when those slots change."""
-    wl = W.config3(block_size=64, num_seqs=6, num_heads=2)
+    wl = W.short_rows(block_size=64, num_seqs=6, num_heads=2)
     a = run_decode(oracle_lib, wl)
     assert np.isfinite(a).all()
     k, v = wl.k_pool.copy(), wl.v_pool.copy()
@@ -216,7 +216,7 @@ def test_unused_slots_never_read(oracle_lib):
 def test_placement_invariance(oracle_lib):
     """Any placement of the same logical blocks gives bit-identical results
     (the kernel only ever sees physical block ids: wywy.jp WHY)."""
-    wl = W.config2(num_seqs=5, num_heads=2)
+    wl = W.opt13b_layer(num_seqs=5, num_heads=2)
     ref = run_decode(oracle_lib, wl)
     for s in range(3):
         r = W.relayout(wl, s)
@@ -227,7 +227,7 @@ def test_placement_invariance(oracle_lib):
 def test_block_size_invariance(oracle_lib):
     """Same logical K/V stored with B = 8, 16, 32, 64: bit-identical output
     (sums run in logical token order whatever the block size)."""
-    base = W.config3(block_size=16, num_seqs=6, num_heads=2)
+    base = W.short_rows(block_size=16, num_seqs=6, num_heads=2)
     ref = run_decode(oracle_lib, base)
     for B in (8, 32, 64):
         r = W.relayout(base, 100 + B, block_size=B)
@@ -236,9 +236,9 @@ def test_block_size_invariance(oracle_lib):
 
 
 def test_shared_versus_copied_prefix(oracle_lib):
-    """Config 4's shared prompt blocks (refcount 6) and copy-on-write copies
+    """The shared prompts' blocks (refcount 6) and copy-on-write copies
     give bit-identical results to every sequence owning private copies."""
-    wl = W.config4(num_prompts=3, samples=6, num_heads=2)
+    wl = W.shared_prompts(num_prompts=3, samples=6, num_heads=2)
     ref = run_decode(oracle_lib, wl)
     private = W.relayout(wl, 5)
     assert np.array_equal(run_decode(oracle_lib, private), ref)
@@ -423,10 +423,10 @@ def test_cow_worked_example(oracle_lib):
         assert np.allclose(out[i], ref.reshape(H, D).numpy(), rtol=0, atol=1e-13)
 
 
-@pytest.mark.parametrize("make", [lambda: W.config1(),
-                                  lambda: W.config4(num_prompts=4, samples=6, num_heads=2),
-                                  lambda: W.config3(block_size=8, num_seqs=10, num_heads=2)],
-                         ids=["cfg1", "cfg4-small", "cfg3-b8-small"])
+@pytest.mark.parametrize("make", [lambda: W.tiny_fp32(),
+                                  lambda: W.shared_prompts(num_prompts=4, samples=6, num_heads=2),
+                                  lambda: W.short_rows(block_size=8, num_seqs=10, num_heads=2)],
+                         ids=["tiny", "cow-small", "short-b8-small"])
 def test_step_reproduces_placement(oracle_lib, make):
     """Pools before the step + the step's copies and writes (oracle) equal, bit
     for bit, the generator's own block-granular placement of the full
@@ -479,7 +479,7 @@ def test_copy_rejects_conflicting_pairs(oracle_lib):
 
 
 def test_bad_table_entry_reported(oracle_lib):
-    wl = W.config1()
+    wl = W.tiny_fp32()
     t = wl.block_tables.copy()
     t[3, 1] = wl.num_blocks
     with pytest.raises(oracle_lib.OracleError):
@@ -496,7 +496,7 @@ def test_split_merge_identity(oracle_lib, part):
     partition, merge with exp(m_p - M) weights: equals the unsplit result
     (ricepunchb 3.3: per-block scores, softmax completed by a final
     reduction).  Written independently here in fp64 numpy."""
-    wl = W.config2(num_seqs=4, num_heads=2)
+    wl = W.opt13b_layer(num_seqs=4, num_heads=2)
     ref = run_decode(oracle_lib, wl)
     for b in range(wl.num_seqs):
         n = int(wl.context_lens[b])
@@ -525,7 +525,7 @@ def test_split_merge_identity(oracle_lib, part):
 
 def swap_workload(seed=12):
     """Config-1 sequences with a host pool of another size to swap into."""
-    wl = W.config1(seed=seed)
+    wl = W.tiny_fp32(seed=seed)
     NB = wl.num_blocks
     nb = [-(-int(c) // wl.block_size) for c in wl.context_lens]
     return wl, NB, nb

@@ -24,17 +24,17 @@ def live_entries(wl):
 
 
 def test_deterministic():
-    a, b = W.config2(num_seqs=8, num_heads=2), W.config2(num_seqs=8, num_heads=2)
+    a, b = W.opt13b_layer(num_seqs=8, num_heads=2), W.opt13b_layer(num_seqs=8, num_heads=2)
     assert np.array_equal(a.context_lens, b.context_lens)
     assert np.array_equal(a.block_tables, b.block_tables)
     assert np.array_equal(a.q.view(np.uint16), b.q.view(np.uint16))
     assert np.array_equal(a.k_pool.view(np.uint16), b.k_pool.view(np.uint16))
-    c = W.config2(seed=99, num_seqs=8, num_heads=2)
+    c = W.opt13b_layer(seed=99, num_seqs=8, num_heads=2)
     assert not np.array_equal(a.context_lens, c.context_lens)
 
 
 def test_config1_recipe():
-    wl = W.config1()
+    wl = W.tiny_fp32()
     assert list(wl.context_lens) == [1, 17, 33, 50, 50]          # 4 sequences + the fork of the 4th
     assert (wl.num_heads, wl.head_dim, wl.block_size, wl.num_blocks) == (2, 64, 16, 32)
     assert wl.dtype == W.F32 and wl.scale == np.float32(1 / 8)
@@ -47,21 +47,21 @@ def test_config1_recipe():
     assert wl.slot_mapping[3] == wl.block_tables[3, 3] * 16 + 49 % 16
 
 
-@pytest.mark.parametrize("make", [lambda: W.config2(num_seqs=16, num_heads=2),
-                                  lambda: W.config3(block_size=8, num_seqs=16, num_heads=2),
-                                  lambda: W.config5(num_seqs=4, num_heads=2)],
-                         ids=["cfg2", "cfg3-b8", "cfg5-meta"])
+@pytest.mark.parametrize("make", [lambda: W.opt13b_layer(num_seqs=16, num_heads=2),
+                                  lambda: W.short_rows(block_size=8, num_seqs=16, num_heads=2),
+                                  lambda: W.long_context(num_seqs=4, num_heads=2)],
+                         ids=["opt13b", "short-b8", "long-meta"])
 def test_scattered_unique_placement(make):
     wl = make()
     live = np.concatenate(live_entries(wl))
     assert live.min() >= 0 and live.max() < wl.num_blocks
-    assert len(np.unique(live)) == len(live)        # no sharing outside config 4
+    assert len(np.unique(live)) == len(live)        # no sharing outside the shared-prompt workload
     assert wl.num_blocks == math.ceil(1.5 * len(live))
     assert len(np.unique(wl.slot_mapping)) == len(wl.slot_mapping)
 
 
 def test_config2_lengths():
-    wl = W.config2(num_heads=1)
+    wl = W.opt13b_layer(num_heads=1)
     ctx = wl.context_lens
     assert ctx.min() >= 1 and ctx.max() <= 2048 and len(ctx) == 64
     big = W.lognormal_lengths(np.random.default_rng(0), 200000)
@@ -70,10 +70,10 @@ def test_config2_lengths():
 
 
 def test_config3_same_logical_values_for_every_block_size():
-    ref = W.config3(block_size=16, num_seqs=6, num_heads=2)
+    ref = W.short_rows(block_size=16, num_seqs=6, num_heads=2)
     assert ref.context_lens.min() >= 20 and ref.context_lens.max() <= 200
     for B in (8, 32, 64):
-        wl = W.config3(block_size=B, num_seqs=6, num_heads=2)
+        wl = W.short_rows(block_size=B, num_seqs=6, num_heads=2)
         assert np.array_equal(wl.context_lens, ref.context_lens)
         assert all(np.array_equal(a.view(np.uint16), b.view(np.uint16))
                    for a, b in zip(wl.logical_k, ref.logical_k))
@@ -81,7 +81,7 @@ def test_config3_same_logical_values_for_every_block_size():
 
 
 def test_config4_sharing_structure():
-    wl = W.config4(num_prompts=5, samples=6, num_heads=2)
+    wl = W.shared_prompts(num_prompts=5, samples=6, num_heads=2)
     P, T = wl.extra["prompt_lens"], wl.extra["tail_lens"]
     assert wl.num_seqs == 30
     refcount = {}
@@ -105,7 +105,7 @@ def test_config4_sharing_structure():
 
 
 def test_unused_slots_hold_nan():
-    wl = W.config2(num_seqs=6, num_heads=2)
+    wl = W.opt13b_layer(num_seqs=6, num_heads=2)
     rows_finite = np.isfinite(wl.k_pool).all(axis=-1)        # [NB][H][B]
     assert rows_finite.sum() == wl.context_lens.sum() * wl.num_heads
     assert np.isnan(wl.k_pool_pre).sum() > np.isnan(wl.k_pool).sum()

@@ -312,7 +312,7 @@ def relayout(wl: Workload, place_seed: int, block_size: int | None = None) -> Wo
                             np.random.default_rng(np.random.SeedSequence([wl.seed, 7, place_seed])))
 
 
-def config1(seed=1, host=True):
+def tiny_fp32(seed=1, host=True):
     return _simple("tiny-fp32", seed, F32, H=2, D=64, B=16, ctx=[1, 17, 33, 50], NB=32, MB=4,
                    host=host, fork_last=True)
 
@@ -322,28 +322,28 @@ def lognormal_lengths(rng, n, median=300.0, sigma=0.9, lo=1, hi=2048):
     return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
 
 
-def config2(seed=2, host=True, num_seqs=64, num_heads=40):
+def opt13b_layer(seed=2, host=True, num_seqs=64, num_heads=40):
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
     ctx = lognormal_lengths(rng, num_seqs)
     return _simple("opt13b-layer", seed, F16, H=num_heads, D=128, B=16, ctx=ctx, MB=2048 // 16,
                    host=host)
 
 
-def config3(seed=3, block_size=16, host=True, num_seqs=256, num_heads=40):
+def short_rows(seed=3, block_size=16, host=True, num_seqs=256, num_heads=40):
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
     ctx = rng.integers(20, 200, size=num_seqs, endpoint=True)
     return _simple(f"short-b{block_size}", seed, F16, H=num_heads, D=128, B=block_size, ctx=ctx,
                    MB=_blocks_for(200, block_size), host=host)
 
 
-def config5(seed=5, host=False, num_seqs=32, num_heads=96, lo=4096, hi=16384):
+def long_context(seed=5, host=False, num_seqs=32, num_heads=96, lo=4096, hi=16384):
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0]))
     ctx = rng.integers(lo, hi, size=num_seqs, endpoint=True)
     return _simple("long-opt175b-layer", seed, F16, H=num_heads, D=128, B=16, ctx=ctx,
                    MB=_blocks_for(hi, 16), host=host)
 
 
-def config4(seed=4, host=True, num_prompts=32, samples=6, num_heads=40,
+def shared_prompts(seed=4, host=True, num_prompts=32, samples=6, num_heads=40,
             prompt_range=(64, 512), tail_range=(1, 256)):
     """Shared prompts with `samples` parallel samples each.  Before the step
     the pool holds only the prompts (their blocks shared by all samples); the
@@ -420,8 +420,9 @@ Workload.k_pool = _lazy_pool("k_pool", "_place_after")
 Workload.v_pool = _lazy_pool("v_pool", "_place_after")
 
 
-def make(config: int, **kw) -> Workload:
-    return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[config](**kw)
+def make(name: str, **kw) -> Workload:
+    return {"tiny": tiny_fp32, "opt13b": opt13b_layer, "short": short_rows, "cow": shared_prompts,
+            "long": long_context}[name](**kw)
 
 
 # ---------------------------------------------------------------------------
