@@ -17,9 +17,11 @@
  *    `stream`, a hipStream_t; the returns of pa_status_string and
  *    pa_last_error; and the pools of pa_swap_blocks, which may also be
  *    pinned host memory).  The
- *    library allocates nothing, frees nothing and keeps no state between
- *    calls apart from a per-thread error description (pa_last_error).  It
- *    is thread-safe.
+ *    kernel entry points allocate nothing (no device memory, no host heap)
+ *    and free nothing; their only state between calls is a per-thread error
+ *    description (pa_last_error).  They are thread-safe.  The host block
+ *    manager of pa_manager.h owns the host memory of each manager object,
+ *    from pa_manager_create to pa_manager_destroy.
  *  - Work is enqueued asynchronously on `stream` (NULL = the default stream);
  *    no call synchronises.  Buffers must stay valid until the work completes.
  *  - Element type codes: PA_F16 (IEEE binary16) or PA_F32.  Query, pools,

@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_manager.cpp"]
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_plan.cpp",
+           "pa_manager.cpp"]
 LIBRARY = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
@@ -32,15 +33,15 @@ def hipcc() -> str:
     return path
 
 
-def command(output: str) -> list[str]:
+def command(output: str, sources=None) -> list[str]:
     return ([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Wall", "-I", os.path.join(ROOT, "include")] + DEVICE_FLAGS +
-            ["-o", output] + [os.path.join(CSRC, s) for s in SOURCES])
+            ["-o", output] + [os.path.join(CSRC, s) for s in (sources or SOURCES)])
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = command(tmp)
+def _compile(library: str, sources, verbose: bool) -> str:
+    tmp = library + ".tmp"
+    cmd = command(tmp, sources)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature; drop that note.
     noise = "is not a recognized feature for this target"
@@ -49,8 +50,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
+    return library
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libpa.so; returns its path."""
+    return _compile(LIBRARY, SOURCES, verbose)
 
 
 if __name__ == "__main__":

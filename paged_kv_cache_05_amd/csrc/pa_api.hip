@@ -5,10 +5,6 @@
 #include <math.h>
 #include <stdio.h>
 
-#include <algorithm>
-#include <atomic>
-#include <vector>
-
 #include "pa.h"
 #include "pa_manager.h"
 #include "pa_kernels.h"
@@ -48,17 +44,9 @@ int effective_partition(int partition_size, int max_context_len) {
 
 bool valid_partition(int part) { return part >= 16 && part <= kMaxPartition && part % 16 == 0; }
 
-int num_partitions(int max_context_len, int part) {
-  return max_context_len <= 0 ? 1 : (max_context_len + part - 1) / part;
-}
-
 // Description of the last HIP error this library saw on the calling thread.
 thread_local char t_detail[384] = "";
 
-// hipGetLastError reports the last failure of any HIP call on the thread,
-// so a launch first takes whatever an earlier call (of the caller, or of a
-// framework around it) left behind; the status read after the launch then
-// belongs to the launch.  Both are described for pa_last_error.
 // True if the GPU can reach p at that address: device memory, or pinned
 // host memory mapped at the same address.  Pageable host memory (which a
 // kernel cannot touch without faulting) and managed memory are refused, and
@@ -83,6 +71,10 @@ bool gpu_reachable(const void *p, const char *what) {
   return false;
 }
 
+// hipGetLastError reports the last failure of any HIP call on the thread,
+// so a launch first takes whatever an earlier call (of the caller, or of a
+// framework around it) left behind; the status read after the launch then
+// belongs to the launch.  Both are described for pa_last_error.
 template <class Launch>
 int launch_checked(const char *what, Launch &&launch) {
   const hipError_t stale = hipGetLastError();
@@ -101,220 +93,22 @@ int launch_checked(const char *what, Launch &&launch) {
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-int clamp_ctx(int32_t c, int max_context_len) {
-  return c < 0 ? 0 : (c > max_context_len ? max_context_len : c);
-}
-
-// Work list from host-side context lengths: every (sequence, partition)
-// with at least one token (one entry for an empty sequence, whose row is
-// zeroed); and the sequences that span several partitions.  Items longer
-// than twice the mean go first, longest first, so that no long item starts
-// late; the rest keep (sequence, partition) order, which keeps neighbouring
-// sequences (for instance parallel samples sharing prompt blocks) close in
-// time and mixes sizes so that concurrently running workgroups stay busy.
-// Waves per workgroup: 8, or 4 when the mean item is shorter than 12
-// 16-token tiles (8 waves would leave most of them one tile or none).
-// Measured on 256 sequences of 20..200 tokens (fused step): 4 waves 12-23%
-// faster than 8 at B = 8 / 16 / 64, and 2-6% faster than 2 waves; 8 waves
-// best on the lognormal batch (median 300 tokens).
-// False when either list would exceed the kernel-argument capacity.
-bool plan_work(const int32_t *host_ctx, int num_seqs, int max_context_len, int part,
-               int block_size, pa::WorkList *items, pa::WorkList *merge_rows, int *waves) {
-  int total = 0;
-  long long tokens = 0;
-  for (int b = 0; b < num_seqs; ++b) {
-    const int c = clamp_ctx(host_ctx[b], max_context_len);
-    total += c == 0 ? 1 : (c + part - 1) / part;
-    tokens += c;
-    if (total > pa::kMaxListed) return false;
-  }
-  struct Entry {
-    int tokens;
-    uint32_t item;
-  };
-  Entry e[pa::kMaxListed];
-  int n = 0;
-  merge_rows->count = 0;
-  for (int b = 0; b < num_seqs; ++b) {
-    const int c = clamp_ctx(host_ctx[b], max_context_len);
-    const int np = c == 0 ? 1 : (c + part - 1) / part;
-    for (int q = 0; q < np; ++q)
-      e[n++] = Entry{std::min(part, c - q * part), ((uint32_t)b << 16) | (uint32_t)q};
-    if (np > 1) merge_rows->item[merge_rows->count++] = (uint32_t)b;
-  }
-  const long long long_item = 2 * tokens / n;  // twice the mean item length
-  Entry *mid = std::stable_partition(
-      e, e + n, [long_item](const Entry &x) { return (long long)x.tokens > long_item; });
-  std::stable_sort(e, mid, [](const Entry &x, const Entry &y) { return x.tokens > y.tokens; });
-  items->count = n;
-  for (int i = 0; i < n; ++i) items->item[i] = e[i].item;
-  constexpr long long kShortItemTokens = 12 * 16;
-  *waves = (long long)n * kShortItemTokens > tokens ? 4 : 8;
-  return true;
-}
-
-// Partition length when the caller leaves it to the library and passes
-// host-side lengths: start from PA_LONG_PARTITION and halve while the batch
-// offers fewer than kPlanTargetItems workgroups' worth of (head, sequence,
-// partition) items, down to kPlanMinPartition, never below what the
-// workspace can hold.
-constexpr long long kPlanTargetItems = 2048;
-constexpr int kPlanMinPartition = 256;
-
-int plan_partition(const int32_t *host_ctx, int num_seqs, int num_heads, int head_dim,
-                   int max_context_len, size_t workspace_bytes, bool have_workspace) {
-  int part = PA_LONG_PARTITION;
-  for (;;) {
-    long long items = 0;
-    for (int b = 0; b < num_seqs; ++b) {
-      const int c = clamp_ctx(host_ctx[b], max_context_len);
-      items += (long long)num_heads * (c == 0 ? 1 : (c + part - 1) / part);
-    }
-    const int next = part / 2;
-    if (items >= kPlanTargetItems || next < kPlanMinPartition) break;
-    const int np = num_partitions(max_context_len, next);
-    if (np > 1 && (!have_workspace ||
-                   pa::decode_workspace_layout(num_seqs, num_heads, head_dim, np).total >
-                       workspace_bytes))
-      break;
-    part = next;
-  }
-  return part;
-}
-
 }  // namespace
 
 extern "C" {
 
-// Work list of the prefill: every (sequence, query tile) that the grid
-// would cover, with its weight (the keys its last query sees), grouped by
-// sequence (see the order below).  False if it has more than kMaxListed
-// entries.
-struct PrefillItem {
-  uint32_t code;   // sequence << 16 | query tile
-  int64_t work;
-};
-
-bool plan_prefill(const int32_t *hqs, const int32_t *hctx, int num_seqs, int max_context_len,
-                  int max_query_len, std::vector<PrefillItem> *out) {
-  const int tile = pa::prefill_query_tile();
-  const int max_tiles = (max_query_len + tile - 1) / tile;
-  std::vector<PrefillItem> &list = *out;
-  list.clear();
-  for (int b = 0; b < num_seqs; ++b) {
-    const int m = hqs[b + 1] - hqs[b];
-    if (m <= 0) continue;
-    const int n = hctx ? std::min(std::max(hctx[b], 0), max_context_len) : m;
-    const int tiles = std::min((m + tile - 1) / tile, max_tiles);
-    for (int t = 0; t < tiles; ++t) {
-      if (list.size() >= (size_t)pa::kMaxListed || b > 0xffff) return false;
-      list.push_back({(uint32_t)b << 16 | (uint32_t)t,
-                      (int64_t)n - m + std::min(m, (t + 1) * tile)});
-    }
-  }
-  // Sequence-major: sequences by their heaviest tile, descending, and each
-  // sequence's tiles heaviest first.  The tiles of one sequence then run
-  // together and share the K/V rows they stream in the L2 (a head's
-  // workgroups all land on one XCD: the grid's fastest index is the head).
-  std::vector<int64_t> seq_work(num_seqs > 0 ? num_seqs : 1, 0);
-  for (const PrefillItem &it : list)
-    seq_work[it.code >> 16] = std::max(seq_work[it.code >> 16], it.work);
-  std::stable_sort(list.begin(), list.end(), [&](const PrefillItem &a, const PrefillItem &b) {
-    const int sa = (int)(a.code >> 16), sb = (int)(b.code >> 16);
-    if (sa != sb) return seq_work[sa] != seq_work[sb] ? seq_work[sa] > seq_work[sb] : sa < sb;
-    return a.work > b.work;
-  });
-  return true;
-}
-
 // Prefill workgroups the current device holds at once (CUs times the
-// kernel's workgroups per CU), cached per device; 0 if unknown.
-int prefill_resident_groups() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      return 0;
-    v = cus * pa::prefill_groups_per_cu();
-    cache[dev].store(v, std::memory_order_relaxed);
+// kernel's workgroups per CU); 0 if unknown.  Queried on every planned call:
+// the runtime answers from its cached device properties.
+static int prefill_resident_groups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return 0;
   }
-  return v;
-}
-
-// Split plan.  When the launch leaves the GPU mostly idle (its tiles times
-// heads fall short of two workgroups per CU), the idle slots take extra key
-// chunks: the tile whose current chunk has the most key tiles gets one more
-// chunk (all heads), if it has at least 48 key tiles, its chunks stay at
-// least 16 key tiles long, it has at most kMaxChunks and workspace slots
-// last.  The chunks of a split tile run side by side and a merge pass
-// combines them.  A launch that already fills the GPU is never split.
-// False when no tile is split or the launch list would not fit: the plain
-// list is used.
-bool plan_prefill_split(const std::vector<PrefillItem> &list, int num_heads, int resident,
-                        size_t slots, pa::SplitList *split, pa::SplitList *merges) {
-  if (list.empty() || resident <= 0 || slots < 2) return false;
-  const int kt = pa::prefill_key_tile();
-  // Measured on 40 heads x 128 (single prompts of 1024..4096 tokens, one or
-  // a few; suffixes of 64..256 queries over 2048..8192 cached tokens):
-  // shorter tiles, shorter chunks or more than two workgroups per CU cost
-  // full prompts time (partial results are fp32 rows of 512 bytes per query
-  // and head, written and read back).
-  constexpr int64_t kMinSplitTiles = 48, kMinChunkTiles = 16;
-  int64_t free_groups = (int64_t)resident * 2 / pa::prefill_groups_per_cu() -
-                        (int64_t)list.size() * num_heads;
-  if (free_groups < num_heads) return false;
-  std::vector<int> chunks(list.size(), 1);
-  std::vector<int64_t> tiles(list.size());
-  for (size_t i = 0; i < list.size(); ++i) tiles[i] = (list[i].work + kt - 1) / kt;
-  // largest current chunk first (tiles / chunks, rounded up)
-  auto chunk_len = [&](size_t i) { return (tiles[i] + chunks[i] - 1) / chunks[i]; };
-  std::vector<size_t> heap(list.size());
-  for (size_t i = 0; i < heap.size(); ++i) heap[i] = i;
-  auto less = [&](size_t a, size_t b) { return chunk_len(a) < chunk_len(b); };
-  std::make_heap(heap.begin(), heap.end(), less);
-  size_t used = 0;
-  while (!heap.empty() && free_groups >= num_heads) {
-    std::pop_heap(heap.begin(), heap.end(), less);
-    const size_t i = heap.back();
-    heap.pop_back();
-    const int nc = chunks[i] + 1;
-    const size_t need = nc == 2 ? 2 : 1;   // slots this step takes
-    if (tiles[i] < kMinSplitTiles || nc > pa::kMaxChunks || tiles[i] / nc < kMinChunkTiles ||
-        used + need > slots)
-      continue;
-    chunks[i] = nc;
-    used += need;
-    free_groups -= num_heads;
-    heap.push_back(i);
-    std::push_heap(heap.begin(), heap.end(), less);
-  }
-  if (used == 0) return false;
-  size_t entries = 0;
-  for (int nc : chunks) entries += nc;
-  if (entries > (size_t)pa::kMaxSplitItems) return false;
-  split->count = 0;
-  merges->count = 0;
-  uint32_t slot = 0;
-  for (size_t i = 0; i < list.size(); ++i) {
-    const int nc = chunks[i];
-    for (int c = 0; c < nc; ++c) {
-      split->item[split->count] = list[i].code;
-      split->part[split->count] =   // each chunk its own slot: slot + c
-          nc > 1 ? ((slot + (uint32_t)c) << 8 | (uint32_t)c << 4 | (uint32_t)(nc - 1)) : 0u;
-      ++split->count;
-    }
-    if (nc > 1) {
-      merges->item[merges->count] = list[i].code;
-      merges->part[merges->count] = slot << 8 | (uint32_t)(nc - 1);
-      ++merges->count;
-      slot += (uint32_t)nc;
-    }
-  }
-  return true;
+  return cus * pa::prefill_groups_per_cu();
 }
 
 size_t pa_prefill_workspace_bytes(int num_heads, int head_dim, int slots) {
@@ -360,16 +154,19 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
   p.max_context_len = max_context_len;
   p.num_query_rows = num_query_rows;
   p.scale_log2 = scale * 1.44269504088896340736f;
-  std::vector<PrefillItem> list;
+  pa::PrefillPlan list;
   const bool listed = host_query_start &&
-                      plan_prefill(host_query_start, host_context_lens, num_seqs,
-                                   max_context_len, max_query_len, &list);
+                      pa::plan_prefill(host_query_start, host_context_lens, num_seqs,
+                                       max_context_len, max_query_len, pa::prefill_query_tile(),
+                                       &list);
   const size_t slot_bytes = pa::prefill_slot_bytes(num_heads, head_dim);
   const size_t slots = workspace ? workspace_bytes / slot_bytes : 0;
   pa::SplitList split, merges;
   const bool is_split =
       listed && slots >= 2 &&
-      plan_prefill_split(list, num_heads, prefill_resident_groups(), slots, &split, &merges);
+      pa::plan_prefill_split(list, num_heads, prefill_resident_groups(),
+                             pa::prefill_groups_per_cu(), pa::prefill_key_tile(), slots, &split,
+                             &merges);
   if (is_split) {
     p.part_o = static_cast<float *>(workspace);
     // [slots][H][128][D] outputs, then [slots][H][128] (max, sum)
@@ -379,8 +176,8 @@ int pa_prefill(void *out, const void *q, const void *k_pool, const void *v_pool,
   }
   pa::WorkList items;
   if (listed && !is_split) {
-    items.count = (int)list.size();
-    for (size_t i = 0; i < list.size(); ++i) items.item[i] = list[i].code;
+    items.count = list.count;
+    for (int i = 0; i < list.count; ++i) items.item[i] = list.item[i].code;
   }
   return launch_checked("pa_prefill", [&] {
     return pa::launch_prefill(p, num_seqs, head_dim, block_size, max_query_len,
@@ -444,7 +241,7 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_heads, int head_dim, int 
   if (num_seqs < 0 || num_heads <= 0 || !supported_head_dim(head_dim) || max_context_len < 0 ||
       !valid_partition(part))
     return (size_t)-1;
-  const int np = num_partitions(max_context_len, part);
+  const int np = pa::num_partitions(max_context_len, part);
   if (np <= 1 || num_seqs == 0) return 0;
   return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, np).total;
 }
@@ -457,8 +254,8 @@ int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int
   const int part = effective_partition(partition_size, max_context_len);
   if (!valid_partition(part)) return PA_ERR_SHAPE;
   if (host_context_lens && partition_size == 0)
-    return plan_partition(host_context_lens, num_seqs, num_heads, head_dim, max_context_len,
-                          workspace_bytes, workspace_bytes > 0);
+    return pa::plan_partition(host_context_lens, num_seqs, num_heads, head_dim,
+                              max_context_len, workspace_bytes, workspace_bytes > 0);
   return part;
 }
 
@@ -477,7 +274,7 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
       !valid_partition(part) || !isfinite(scale) || num_seqs > kGridYZ || num_heads > kGridYZ ||
-      num_partitions(max_context_len, part) > kGridYZ)
+      pa::num_partitions(max_context_len, part) > kGridYZ)
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_NULL;
@@ -491,9 +288,8 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
       return PA_ERR_SHAPE;
   }
   if (host_context_lens && partition_size == 0)
-    part = plan_partition(host_context_lens, num_seqs, num_heads, head_dim, max_context_len,
-                          workspace_bytes, workspace != nullptr);
-
+    part = pa::plan_partition(host_context_lens, num_seqs, num_heads, head_dim,
+                              max_context_len, workspace_bytes, workspace != nullptr);
   pa::DecodeParams p{};
   p.out = out;
   p.q = q;
@@ -507,7 +303,7 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
   p.partition_size = part;
-  p.num_partitions = num_partitions(max_context_len, part);
+  p.num_partitions = pa::num_partitions(max_context_len, part);
   p.scale_log2 = scale * 1.44269504088896340736f;
   p.new_key = new_key;
   p.new_value = new_value;
@@ -524,8 +320,8 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
   if (host_context_lens) {
     pa::WorkList items, merge_rows;
     int waves = 8;
-    if (plan_work(host_context_lens, num_seqs, max_context_len, part, block_size, &items,
-                  &merge_rows, &waves))
+    if (pa::plan_work(host_context_lens, num_seqs, max_context_len, part, &items, &merge_rows,
+                      &waves))
       return launch_checked(what, [&] {
         return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, &items, &merge_rows,
                                  waves, static_cast<hipStream_t>(stream));

@@ -283,6 +283,10 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   // Fold one tile into the row state.  kMask: the tile may hold tokens at or
   // past tok_end, which are excluded by select.
   auto consume = [&](Tile<T, D> &tile, int ts, auto mask_tag) {
+    // No contraction here: fused into the exponent, score * scale - max
+    // would skip the rounding of the product, and the best token's weight
+    // would be 2^(that rounding error) instead of exactly 1.
+#pragma clang fp contract(off)
     constexpr bool kMask = decltype(mask_tag)::value;
     float s[G::kGroups];
 #pragma unroll
@@ -678,20 +682,7 @@ hipError_t launch_dim(const DecodeParams &p, int num_seqs, int head_dim, int blo
   return hipErrorInvalidValue;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
-
-WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_dim,
-                                        int num_partitions) {
-  WorkspaceLayout w{};
-  const size_t rows = (size_t)num_seqs * num_heads;
-  const size_t parts = rows * (size_t)num_partitions;
-  w.ml_off = 0;
-  w.o_off = align256(parts * sizeof(float2));
-  w.total = w.o_off + align256(parts * (size_t)head_dim * sizeof(float));
-  return w;
-}
 
 hipError_t launch_decode(const DecodeParams &p, int num_seqs, int head_dim, int block_size,
                          int dtype, const WorkList *items, const WorkList *merge_rows,

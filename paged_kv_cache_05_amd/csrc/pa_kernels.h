@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa_plan.h"
+
 namespace pa {
 
 // Everything the decode kernel reads besides its template parameters.
@@ -32,22 +34,6 @@ struct DecodeParams {
   const void *new_key;
   const void *new_value;
   const int64_t *slot_mapping;
-};
-
-// Workspace carve-up shared by the size query and the launch.
-struct WorkspaceLayout {
-  size_t ml_off, o_off, total;
-};
-WorkspaceLayout decode_workspace_layout(int num_seqs, int num_heads, int head_dim,
-                                        int num_partitions);
-
-// A host-built work list, passed by value as kernel arguments (so it must
-// stay under the 4 KiB argument limit together with DecodeParams).  Each
-// entry packs (sequence << 16) | partition.
-constexpr int kMaxListed = 960;
-struct WorkList {
-  int count;
-  uint32_t item[kMaxListed];
 };
 
 // dtype: 0 = f16, 1 = f32.  `items` (optional) lists the (sequence,

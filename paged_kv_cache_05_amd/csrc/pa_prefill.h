@@ -28,19 +28,6 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// Launch list of the split form: each entry is one workgroup's (sequence,
-// query tile) and its key chunk; part = slot << 8 | chunk << 4 |
-// (chunks - 1) with the chunk's own workspace slot, 0 for a whole tile.  A
-// tile's chunks use consecutive slots.  The merge list holds one entry per
-// split tile: part = slot << 8 | (chunks - 1), slot being its first chunk's.
-constexpr int kMaxSplitItems = 448;
-constexpr int kMaxChunks = 16;
-struct SplitList {
-  int count;
-  uint32_t item[kMaxSplitItems];   // sequence << 16 | query tile
-  uint32_t part[kMaxSplitItems];
-};
-
 int prefill_query_tile();
 int prefill_key_tile();
 // Workspace bytes of one partial-result slot.

@@ -147,33 +147,50 @@ def test_block_size_sweep(pa, oracle_lib, device, B):
         assert np.array_equal(bits(got), bits(ref))
 
 
-def test_long_context_sampled(pa, oracle_lib, device):
-    """OPT-175B layer shape, all 96 heads, contexts 4K-16K: the full batch on the
-    GPU (device-filled pools), checked against the oracle on sampled rows with
-    the real block table."""
+def test_long_context_every_row(pa, oracle_lib, device):
+    """OPT-175B layer shape, all 96 heads, contexts 4K-16K (device-filled
+    pools): every (sequence, head) row of four launches against the oracle --
+    the bench's fused step (pa_decode_append, host-planned), then pa_decode
+    on the pools it wrote through the grid launch (default partition 4096,
+    merged), the host-planned list (partition planned from the lengths) and
+    the grid at partition 1024.  The oracle runs per sequence on that
+    sequence's blocks, copied to the host one sequence at a time."""
     wl = W.long_context(host=False)
-    announce(f"{wl.name}: N={wl.num_seqs} H={wl.num_heads} NB={wl.num_blocks} filling pools")
+    N, H, D = wl.q.shape
+    announce(f"{wl.name}: N={N} H={H} NB={wl.num_blocks} filling pools")
     k, v = W.device_pools(wl, device)
-    announce(f"{wl.name}: pa_decode default partition")
-    got = gpu_decode(pa, wl, k, v, device)
-    rng = np.random.default_rng(55)
-    rows = [(int(b), int(h)) for b, h in zip(rng.integers(0, wl.num_seqs, 8),
-                                             rng.integers(0, wl.num_heads, 8))]
-    rows.append((int(np.argmax(wl.context_lens)), 0))
-    for b, h in rows:
+    q, tables, ctx = dev(wl.q, device), dev(wl.block_tables, device), dev(wl.context_lens, device)
+    maxctx = wl.max_context_len
+    scale = float(wl.scale)
+    outs = {}
+    announce(f"{wl.name}: fused step, host-planned")
+    ws = pa.new_workspace(N, H, D, maxctx, 256, device=device)
+    o = torch.empty_like(q)
+    pa.pa_decode_append(o, q, dev(wl.new_key, device), dev(wl.new_value, device), k, v, tables,
+                        ctx, dev(wl.slot_mapping, device), scale, maxctx, 0, ws,
+                        host_context_lens=wl.context_lens)
+    outs["fused listed"] = o
+    for name, part, host in (("grid default", 0, None), ("listed", 0, wl.context_lens),
+                             ("grid 1024", 1024, None)):
+        announce(f"{wl.name}: pa_decode {name}")
+        o = torch.empty_like(q)
+        w = pa.new_workspace(N, H, D, maxctx, part if host is None else 256, device=device)
+        pa.pa_decode(o, q, k, v, tables, ctx, scale, maxctx, partition_size=part, workspace=w,
+                     host_context_lens=host)
+        outs[name] = o
+    torch.cuda.synchronize()
+    got = {name: o.cpu().numpy() for name, o in outs.items()}
+    for b in range(N):
         n = int(wl.context_lens[b])
-        blocks = wl.block_tables[b, :-(-n // 16)].astype(np.int64)
-        kh = np.full((wl.num_blocks, 1, 16, 128), np.nan, np.float16)
-        vh = kh.copy()
-        idx = torch.as_tensor(blocks, device=device)
-        kh[blocks] = k[idx, h:h + 1].cpu().numpy()
-        vh[blocks] = v[idx, h:h + 1].cpu().numpy()
-        ref = oracle_lib.decode(wl.q[b:b + 1, h:h + 1], kh, vh, wl.block_tables[b:b + 1],
+        nblk = -(-n // wl.block_size)
+        idx = torch.as_tensor(wl.block_tables[b, :nblk].astype(np.int64), device=device)
+        kb, vb = k[idx].cpu().numpy(), v[idx].cpu().numpy()
+        ref = oracle_lib.decode(wl.q[b:b + 1], kb, vb, np.arange(nblk, dtype=np.int32)[None],
                                 wl.context_lens[b:b + 1], wl.scale)
-        assert_close(got[b:b + 1, h:h + 1], ref, wl.dtype, f"{wl.name} row ({b},{h}) ctx={n}")
-    announce(f"{wl.name}: partition 1024 agrees")
-    got2 = gpu_decode(pa, wl, k, v, device, partition_size=1024)
-    assert np.abs(got2.astype(np.float64) - got.astype(np.float64)).max() <= 2e-3
+        for name, g in got.items():
+            assert_close(g[b:b + 1], ref, wl.dtype, f"{wl.name} {name} sequence {b} ctx={n}")
+        if b % 8 == 7:
+            announce(f"{wl.name}: {b + 1} of {N} sequences match the oracle on every head")
     del k, v
     torch.cuda.empty_cache()
 

@@ -300,36 +300,17 @@ def test_prefill_no_split_when_balanced(pa, oracle_lib, device):
     assert np.array_equal(got.view(np.uint16), listed.view(np.uint16))
 
 
-def sampled_rows(wl, per_seq, rng):
-    """(sequence, first row, count) windows whose oracle values need only a
-    truncated context: a query at position p sees tokens 0..p."""
-    out = []
-    for b in range(wl.num_seqs):
-        m = int(wl.query_lens[b])
-        if m == 0:
-            continue
-        starts = {0, max(m - per_seq, 0)} | {int(x) for x in rng.integers(0, m, size=2)}
-        for s in sorted(starts):
-            out.append((b, s, min(per_seq, m - s)))
-    return out
-
-
 @pytest.mark.parametrize("which", ["mix", "shared"])
-def test_prefill_full_size_sampled(pa, oracle_lib, device, which):
-    """The OPT-13B-shaped workloads (40 heads x 128, B 16) in one launch;
-    windows of rows checked against the oracle on truncated contexts."""
+def test_prefill_full_size_every_row(pa, oracle_lib, device, which):
+    """The OPT-13B-shaped workloads (40 heads x 128, B 16) in one launch:
+    every query row of every head against the oracle."""
     announce(f"prefill full size {which}")
     wl = W.prefill_mix() if which == "mix" else W.prefill_shared()
     got = run_gpu(pa, wl, device, listed=True)
-    rng = np.random.default_rng(17)
-    for b, s, k in sampled_rows(wl, 6, rng):
-        n, m = int(wl.context_lens[b]), int(wl.query_lens[b])
-        qs = int(wl.query_start[b])
-        n_cut = n - m + s + k                    # context through the window's last query
-        ref = oracle_lib.prefill(wl.q[qs + s:qs + s + k], wl.k_pool, wl.v_pool,
-                                 wl.block_tables[b:b + 1], np.array([n_cut], np.int32),
-                                 np.array([0, k], np.int32), wl.scale)
-        check(got[qs + s:qs + s + k], ref, f"sequence {b} rows {s}..{s + k - 1}")
+    announce(f"prefill full size {which}: oracle over {int(wl.query_start[-1])} query rows")
+    ref = oracle_lib.prefill(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    check(got, ref, f"prefill {which}")
 
 
 @pytest.mark.parametrize("split", [False, True], ids=["listed", "split"])
