@@ -17,11 +17,13 @@
  *    `stream`, a hipStream_t; the returns of pa_status_string and
  *    pa_last_error; and the pools of pa_swap_blocks, which may also be
  *    pinned host memory).  The
- *    kernel entry points allocate nothing (no device memory, no host heap)
- *    and free nothing; their only state between calls is a per-thread error
- *    description (pa_last_error).  They are thread-safe.  The host block
- *    manager of pa_manager.h owns the host memory of each manager object,
- *    from pa_manager_create to pa_manager_destroy.
+ *    kernel entry points allocate nothing and free nothing.  Their only
+ *    state between calls is a per-thread error description (pa_last_error)
+ *    and, for pa_decode_noalloc alone, a static device array per GPU and its
+ *    device address, looked up once per GPU.  They are thread-safe
+ *    (pa_decode_noalloc calls that overlap on one GPU race on its array).
+ *    The host block manager of pa_manager.h owns the host memory of each
+ *    manager object, from pa_manager_create to pa_manager_destroy.
  *  - Work is enqueued asynchronously on `stream` (NULL = the default stream);
  *    no call synchronises.  Buffers must stay valid until the work completes.
  *  - Element type codes: PA_F16 (IEEE binary16) or PA_F32.  Query, pools,
@@ -161,6 +163,41 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
               float scale, int dtype, int partition_size,
               const int32_t *host_context_lens,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Size of the static device scratch that pa_decode_noalloc uses: one array
+ * of this many bytes on each GPU the library runs on, held until the
+ * process ends.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same arguments as pa_decode minus the workspace, and the same result, bit
+ * for bit, as pa_decode with those arguments and a workspace of
+ * PA_NOALLOC_SCRATCH_BYTES.  The partial results of rows that span several
+ * partitions go to a static device array of PA_NOALLOC_SCRATCH_BYTES per
+ * GPU instead of a caller's workspace.  The call allocates nothing (no
+ * hipMalloc, no host heap); its first call on a device looks up the
+ * array's address there (hipGetSymbolAddress), and later calls reuse it.
+ *
+ * A batch whose partial results need more than PA_NOALLOC_SCRATCH_BYTES
+ * (num_seqs * num_heads * partitions * (head_dim + 2) * 4 bytes, each part
+ * 256-byte aligned; at most 32263 (sequence, head, partition) rows at
+ * head_dim 128, 63550 at head_dim 64) returns PA_ERR_WORKSPACE before any launch, with the sizes
+ * in pa_last_error; with host_context_lens and partition_size 0 the planner
+ * picks a partition length that fits when one exists.  Every call on a GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be ordered
+ * by the caller.  The array's contents from an earlier call do not matter.
+ */
+int pa_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int num_seqs, int num_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_context_len,
+                      float scale, int dtype, int partition_size,
+                      const int32_t *host_context_lens, void *stream);
 
 /*
  * Store each new token's K and V rows, all heads, in its slot ([wywy]

@@ -7,6 +7,8 @@ carry the C names:
 
 * :func:`pa_decode` -- single-query decode attention over block pools
   addressed through per-sequence block tables,
+* :func:`pa_decode_noalloc` -- pa_decode without a workspace (static device
+  scratch), for callers that cannot allocate,
 * :func:`pa_decode_append` -- one fused step: store each new token's K/V and
   decode over the context that includes it,
 * :func:`pa_prefill` -- causal attention of a chunk of query tokens per
@@ -38,6 +40,7 @@ PA_F32 = 1
 PA_DEFAULT_PARTITION = 1024
 PA_LONG_PARTITION = 4096
 PA_LONG_CONTEXT = 8192
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def default_partition(max_context_len: int) -> int:
@@ -45,7 +48,7 @@ def default_partition(max_context_len: int) -> int:
     return PA_LONG_PARTITION if max_context_len > PA_LONG_CONTEXT else PA_DEFAULT_PARTITION
 
 # Every symbol include/pa.h and include/pa_manager.h declare.
-EXPORTS = ("pa_decode", "pa_decode_append", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
+EXPORTS = ("pa_decode", "pa_decode_append", "pa_decode_noalloc", "pa_decode_workspace_bytes", "pa_decode_partition_size", "pa_write_kv",
            "pa_copy_blocks", "pa_swap_blocks", "pa_prefill", "pa_prefill_workspace_bytes",
            "pa_status_string", "pa_last_error",
            "pa_manager_create", "pa_manager_destroy", "pa_manager_add", "pa_manager_fork",
@@ -93,6 +96,9 @@ def library() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                               f32, i32, i32, vp, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      f32, i32, i32, vp, vp]
+    lib.pa_decode_noalloc.restype = i32
     lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      i32, i32, f32, i32, i32, vp, vp, sz, vp]
     lib.pa_decode_append.restype = i32
@@ -253,6 +259,23 @@ def pa_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, max_con
         int(partition_size), None if host is None else host.ctypes.data, ws_ptr, ws_bytes,
         _stream(stream))
     _check(rc, "pa_decode")
+    return out
+
+
+def pa_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      max_context_len, partition_size=0, stream=None, host_context_lens=None):
+    """pa_decode without a workspace: partial results go to the library's
+    static device scratch (PA_NOALLOC_SCRATCH_BYTES per GPU), so the call
+    allocates nothing.  Calls that overlap on one GPU race on that scratch."""
+    import torch
+    host, (N, H, D, B, NB) = _decode_common(q, out, k_pool, v_pool, block_tables, context_lens,
+                                            host_context_lens)
+    rc = library().pa_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        N, H, D, B, NB, block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(q),
+        int(partition_size), None if host is None else host.ctypes.data, _stream(stream))
+    _check(rc, "pa_decode_noalloc")
     return out
 
 

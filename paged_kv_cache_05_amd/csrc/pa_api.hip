@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "pa.h"
 #include "pa_manager.h"
 #include "pa_kernels.h"
@@ -259,15 +261,55 @@ int pa_decode_partition_size(const int32_t *host_context_lens, int num_seqs, int
   return part;
 }
 
-// pa_decode and pa_decode_append: the append arguments are all null for a
-// plain decode.
+// Allocation-free decode (pa_decode_noalloc): the partial results of rows
+// that span several partitions live in this file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept in g_scratch.  Calls that overlap on one GPU share the array and
+// race; nothing in it needs clearing (the kernels write every partial
+// result before the merge reads it).
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+static constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, or null with the
+// reason in pa_last_error.
+static void *scratch_on_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    snprintf(t_detail, sizeof t_detail, "pa_decode_noalloc: no usable current device (%s, %d)",
+             hipGetErrorName(e), dev);
+    return nullptr;
+  }
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    snprintf(t_detail, sizeof t_detail,
+             "pa_decode_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: "
+             "%s (%s)",
+             dev, hipGetErrorName(e), hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch[dev].store(ptr, std::memory_order_release);   // same value if two threads race
+  return ptr;
+}
+
+// pa_decode, pa_decode_append and pa_decode_noalloc: the append arguments
+// are all null for a plain decode; static_scratch selects the
+// allocation-free form (workspace arguments ignored).
 static int decode_impl(const char *what, void *out, const void *q, const void *new_key,
                        const void *new_value, const void *k_pool, const void *v_pool,
                        const int32_t *block_tables, const int32_t *context_lens,
                        const int64_t *slot_mapping, int num_seqs, int num_heads, int head_dim,
                        int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len,
                        float scale, int dtype, int partition_size, const int32_t *host_context_lens,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+                       void *workspace, size_t workspace_bytes, void *stream,
+                       bool static_scratch = false) {
   int rc = check_pool(num_heads, head_dim, block_size, num_blocks, dtype);
   if (rc != PA_OK) return rc;
   int part = effective_partition(partition_size, max_context_len);
@@ -287,9 +329,29 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
     if (!aligned16(new_key) || !aligned16(new_value) || ((uintptr_t)slot_mapping & 7u))
       return PA_ERR_SHAPE;
   }
+  if (static_scratch) {
+    workspace = scratch_on_current_device();
+    if (!workspace) return PA_ERR_HIP;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
   if (host_context_lens && partition_size == 0)
     part = pa::plan_partition(host_context_lens, num_seqs, num_heads, head_dim,
                               max_context_len, workspace_bytes, workspace != nullptr);
+  if (static_scratch) {
+    const int np = pa::num_partitions(max_context_len, part);
+    const size_t need = np > 1 ? pa::decode_workspace_layout(num_seqs, num_heads, head_dim,
+                                                             np).total
+                               : 0;
+    if (need > PA_NOALLOC_SCRATCH_BYTES) {
+      snprintf(t_detail, sizeof t_detail,
+               "pa_decode_noalloc: %d sequences x %d heads x %d partitions of %d tokens need "
+               "%zu bytes of partial results; the static scratch holds %zu (use a longer "
+               "partition_size, or pa_decode with a workspace)",
+               num_seqs, num_heads, np, part, need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+      return PA_ERR_WORKSPACE;
+    }
+  }
+
   pa::DecodeParams p{};
   p.out = out;
   p.q = q;
@@ -343,6 +405,17 @@ int pa_decode(void *out, const void *q, const void *k_pool, const void *v_pool,
                      context_lens, nullptr, num_seqs, num_heads, head_dim, block_size,
                      num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                      partition_size, host_context_lens, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                      const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                      int num_heads, int head_dim, int block_size, int num_blocks,
+                      int max_blocks_per_seq, int max_context_len, float scale, int dtype,
+                      int partition_size, const int32_t *host_context_lens, void *stream) {
+  return decode_impl("pa_decode_noalloc", out, q, nullptr, nullptr, k_pool, v_pool,
+                     block_tables, context_lens, nullptr, num_seqs, num_heads, head_dim,
+                     block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                     partition_size, host_context_lens, nullptr, 0, stream, true);
 }
 
 int pa_decode_append(void *out, const void *q, const void *new_key, const void *new_value,

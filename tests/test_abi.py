@@ -45,6 +45,8 @@ def test_header_constants_match_binding(pa):
     assert int(consts["PA_DEFAULT_PARTITION"]) == pa.PA_DEFAULT_PARTITION
     assert int(consts["PA_LONG_PARTITION"]) == pa.PA_LONG_PARTITION
     assert int(consts["PA_LONG_CONTEXT"]) == pa.PA_LONG_CONTEXT
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m[1]) << int(m[2]) == pa.PA_NOALLOC_SCRATCH_BYTES
 
 
 def test_status_strings(pa):
@@ -146,6 +148,36 @@ def decode_call(lib, **over):
 ])
 def test_decode_rejects(pa, over, code):
     assert decode_call(pa.library(), **over) == code
+
+
+def noalloc_call(lib, **over):
+    args = dict(out=OUT, q=Q, k_pool=KP, v_pool=VP, block_tables=TB, context_lens=CL,
+                num_seqs=4, num_heads=2, head_dim=64, block_size=16, num_blocks=32,
+                max_blocks_per_seq=4, max_context_len=50, scale=0.125, dtype=1,
+                partition_size=0, host_context_lens=None, stream=None)
+    args.update(over)
+    return lib.pa_decode_noalloc(*args.values())
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(block_tables=None), -1),
+    (dict(head_dim=96), -3), (dict(block_size=12), -3), (dict(dtype=2), -3),
+    (dict(num_heads=0), -2), (dict(num_seqs=-1), -2), (dict(max_context_len=65), -2),
+    (dict(partition_size=24), -2), (dict(scale=float("nan")), -2), (dict(q=Q + 8), -2),
+    (dict(num_seqs=0, out=None), 0),
+])
+def test_noalloc_rejects(pa, over, code):
+    assert noalloc_call(pa.library(), **over) == code
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+def test_noalloc_without_a_device_reports_it(pa):
+    """Valid arguments and no GPU: the scratch's device address cannot be
+    looked up, so the call returns PA_ERR_HIP before any launch, and
+    pa_last_error says why."""
+    assert noalloc_call(pa.library()) == -5
+    assert "pa_decode_noalloc" in pa.pa_last_error()
 
 
 def prefill_call(lib, **over):
