@@ -181,7 +181,7 @@ def bench_prefill(args):
     launch_tflops = mix["flops"] / (mix["per_call"] * 1e-3) / 1e12
 
     cpu = None
-    if not args.no_cpu_baseline and default_config:
+    if not args.no_cpu_baseline:
         import oracle
         if not os.path.exists(oracle.LIBRARY):
             oracle.build()
@@ -479,11 +479,14 @@ def main():
                          "pa_decode_append")
     ap.add_argument("--no-host-lengths", action="store_true",
                     help="do not pass host-side context lengths to pa_decode")
-    ap.add_argument("--config", choices=["opt13b", "short", "long"], default="opt13b",
+    ap.add_argument("--config", choices=["opt13b", "short", "long", "cow"], default="opt13b",
                     help="decode workload: opt13b (the default line: 64 seqs x 40 heads, "
                          "lognormal contexts), short (256 seqs of 20-200 tokens), long (32 seqs "
-                         "x 96 heads of 4096-16384 tokens); the CPU baseline and the stored HBM "
-                         "counters cover opt13b only")
+                         "x 96 heads of 4096-16384 tokens), cow (32 prompts x 6 samples sharing "
+                         "prompt blocks: copy, write and decode timed apart and together); the "
+                         "CPU baseline and the stored HBM counters cover opt13b only")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the reference stream and gather reads")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
                     help="block size of the short workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -510,6 +513,142 @@ def main():
     if args.workload == "prefill":
         return bench_prefill(args)
 
+    if args.config == "cow":
+        return bench_cow(args)
+    return bench_decode(args)
+
+
+def bench_lib():
+    """libpa_bench.so (the reference read kernels, include/pa_bench.h), loaded
+    after torch and libpa.so so that it binds to torch's HIP runtime."""
+    import ctypes
+
+    import paged_kv_cache_05_amd as pa
+    pa.library()
+    path = os.path.join(ROOT, "paged_kv_cache_05_amd", "libpa_bench.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"bench: {path} is not built (python -m paged_kv_cache_05_amd._build)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.pa_bench_stream_read.argtypes = [vp, sz, i32, i32, vp, vp]
+    lib.pa_bench_stream_read.restype = i32
+    lib.pa_bench_gather_read.argtypes = [vp, vp, sz, vp, i32, i32, vp, vp]
+    lib.pa_bench_gather_read.restype = i32
+    return lib
+
+
+def tile_offsets(wl):
+    """Byte offsets of every (block, head) tile a decode of `wl` reads, once
+    per distinct block: (phys * H + h) * B * D * element bytes."""
+    import workloads as W
+    ids, _ = W.live_rows(wl)
+    H, B, D, s = wl.num_heads, wl.block_size, wl.head_dim, wl.elem_bytes
+    off = (ids[:, None] * H + np.arange(H)[None, :]) * (B * D * s)
+    return off.reshape(-1).astype(np.int64)
+
+
+def reference_reads(wl, pools, reps):
+    """The bandwidth ceilings the decode is read against, measured live:
+    (a) a stream over a 4 GiB buffer, non-temporal 16-byte loads, the best
+    of six launch shapes (1024 / 2048 / 4096 workgroups of 256 threads, one
+    or four loads per thread in flight); (b) a gather of exactly the workload's
+    (block, head) tiles of K and V at their places in the rotated layer
+    pools, one wave per tile, the same loads.  Events around every launch."""
+    import torch
+    lib = bench_lib()
+    device = pools[0][0].device
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=device)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+
+    def stream_with(grid, unroll):
+        def once(_):
+            rc = lib.pa_bench_stream_read(buf.data_ptr(), nbytes, grid, unroll, sink.data_ptr(),
+                                          stream.cuda_stream)
+            if rc != 0:
+                raise SystemExit(f"bench: pa_bench_stream_read returned {rc}")
+        return once
+
+    # a few launch shapes; the ceiling is the best of them
+    shapes = {f"{g}x256 threads, {u} KiB/wave in flight": (g, u)
+              for g in (1024, 2048, 4096) for u in (1, 4)}
+    stream_rates = {name: nbytes / timed(stream_with(*gu), max(3, reps // 20)) / 1e9
+                    for name, gu in shapes.items()}
+    best = max(stream_rates, key=stream_rates.get)
+    del buf
+    torch.cuda.empty_cache()
+    offs = torch.from_numpy(tile_offsets(wl)).to(device)
+    piece = wl.block_size * wl.head_dim * wl.elem_bytes
+    pool_bytes = pools[0][0].numel() * pools[0][0].element_size()
+
+    def gather_once(i):
+        k, v = pools[i % len(pools)]
+        rc = lib.pa_bench_gather_read(k.data_ptr(), v.data_ptr(), pool_bytes, offs.data_ptr(),
+                                      offs.numel(), piece, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise SystemExit(f"bench: pa_bench_gather_read returned {rc}")
+
+    t_gather = timed(gather_once, reps)
+    gather_bytes = 2 * offs.numel() * piece
+    return {"stream_GBps": round(stream_rates[best], 1), "stream_bytes": nbytes,
+            "stream_best_shape": best,
+            "stream_GBps_by_shape": {k: round(v, 1) for k, v in stream_rates.items()},
+            "gather_GBps": round(gather_bytes / t_gather / 1e9, 1),
+            "gather_bytes": gather_bytes, "gather_pieces": int(offs.numel()),
+            "gather_ms": round(t_gather * 1e3, 5),
+            "what": "stream: 4 GiB read once, best of six launch shapes; gather: this "
+                    "workload's (block, head) K and V tiles (whole blocks) at their places in "
+                    "the rotated layer pools, one wave per tile"}
+
+
+def single_thread_oracle(pools0, wl_default):
+    """The oracle on one thread for the first three configurations (the
+    tiny fp32 batch, the OPT-13B layer of this run, the short-request batch
+    at B = 16): seconds per full decode call."""
+    import oracle
+    import workloads as W
+    import torch
+    res = {}
+    tiny = W.tiny_fp32()
+    t = time.perf_counter()
+    oracle.decode(tiny.q, tiny.k_pool, tiny.v_pool, tiny.block_tables, tiny.context_lens,
+                  tiny.scale, threads=1)
+    res["tiny_fp32_s"] = round(time.perf_counter() - t, 5)
+    kh, vh = pools0[0].cpu().numpy(), pools0[1].cpu().numpy()
+    t = time.perf_counter()
+    oracle.decode(wl_default.q, kh, vh, wl_default.block_tables, wl_default.context_lens,
+                  wl_default.scale, threads=1)
+    res["opt13b_layer_s"] = round(time.perf_counter() - t, 3)
+    short = W.short_rows(block_size=16, host=False)
+    sk, sv = W.device_pools(short, pools0[0].device)
+    skh, svh = sk.cpu().numpy(), sv.cpu().numpy()
+    del sk, sv
+    torch.cuda.empty_cache()
+    t = time.perf_counter()
+    oracle.decode(short.q, skh, svh, short.block_tables, short.context_lens, short.scale,
+                  threads=1)
+    res["short_rows_s"] = round(time.perf_counter() - t, 3)
+    res["opt13b_layer_GBps"] = round(wl_default.algorithmic_bytes() / res["opt13b_layer_s"] / 1e9, 3)
+    res["short_rows_GBps"] = round(short.algorithmic_bytes() / res["short_rows_s"] / 1e9, 3)
+    return res
+
+
+def bench_decode(args):
     import torch
 
     import paged_kv_cache_05_amd as pa
@@ -534,7 +673,7 @@ def main():
     new_k, new_v, slots = dev(wl.new_key), dev(wl.new_value), dev(wl.slot_mapping)
     copies = dev(wl.block_mapping)
     maxctx = wl.max_context_len
-    ws = pa.new_workspace(N, H, D, maxctx, args.partition, device=device)
+    ws = pa.new_workspace(N, H, D, maxctx, args.partition or 256, device=device)
     scale = float(wl.scale)
     # The step's scheduler knows every context length on the host; passing
     # them lets pa_decode launch only non-empty work items, largest first.
@@ -551,12 +690,15 @@ def main():
         ("" if args.split_step else " (fused append: pa_decode_append)")
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev=None, plain=False):
         k, v = pools[i % L]
         pa.pa_copy_blocks(k, v, copies)              # no pairs in this workload: no launch
         if ev is not None:
             ev[0].record(stream)
-        if args.split_step:
+        if plain:
+            pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws,
+                         host_context_lens=host_ctx)
+        elif args.split_step:
             pa.pa_write_kv(new_k, new_v, k, v, slots)
             pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, args.partition, ws,
                          host_context_lens=host_ctx)
@@ -585,12 +727,18 @@ def main():
     # A second pass of K steps with HIP events around every decode launch,
     # for the kernel's average launch duration (the roofline); its events
     # are kept out of the timed region above.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for i in range(K):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    def event_pass(plain):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for i in range(K):
+            step(i, evs[i], plain=plain)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    dec_ms = event_pass(False)
+    # A third pass: pa_decode alone (no new-row store), the call the
+    # bandwidth target names.
+    plain_ms = event_pass(True)
 
     # The same steps replayed from a HIP graph (one captured step per layer
     # pool), as a serving loop that captures its launches would run them.
@@ -612,18 +760,19 @@ def main():
         graph_ms = ga.elapsed_time(gb) / (reps * L)
         del g
 
+    # the benchmark spec's byte count: every context token's K and V row for every
+    # head, plus one 4-byte table entry per block in use.  The step also
+    # stores each sequence's new K/V rows once (reported, not credited).
     decode_bytes = wl.algorithmic_bytes()
-    # the step's necessary traffic: every context token's K and V once (the
-    # new one from its input row), q, out, and the new rows stored once
-    step_bytes = decode_bytes + 2 * N * H * D * wl.elem_bytes
-    # the timed launch: the fused kernel does the whole step; the split form
-    # times pa_decode alone
-    call_bytes = decode_bytes if args.split_step else step_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    new_rows_bytes = 2 * N * H * D * wl.elem_bytes
+    value = decode_bytes / (ms_per_step * 1e-3) / 1e9
     dec_mean = float(dec_ms.mean())
-    achieved = call_bytes / (dec_mean * 1e-3) / 1e9
+    plain_mean = float(plain_ms.mean())
+    achieved = decode_bytes / (dec_mean * 1e-3) / 1e9
     # the stored counters cover the default workload's fused call only
     traffic = None if args.split_step or not default_config else measured_traffic()
+
+    refs = reference_reads(wl, pools, max(20, min(K, 100))) if not args.no_reference else None
 
     # Output of layer 0 for the parity sample and the CPU baseline.
     k0, v0 = pools[0]
@@ -649,7 +798,8 @@ def main():
                "kind": "oracle",
                "sample": f"one full decode call of layer 0 ({N} seqs x {H} heads, "
                          f"sum ctx {int(wl.context_lens.sum())}), fp64, {secs:.2f} s; "
-                         f"{1.0 / secs:.3f} decode steps/s"}
+                         f"{1.0 / secs:.3f} decode steps/s",
+               "single_thread": single_thread_oracle((k0, v0), wl)}
         err = np.abs(gpu_out - ref)
         parity = bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
 
@@ -664,7 +814,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16" if wl.dtype == W.F16 else "f32",
         "data": "synthetic (seeded context lengths, N(0,1) q/K/V, scattered blocks)",
         "config": {
             "workload": {"opt13b": "OPT-13B-shaped single-layer decode step",
@@ -680,14 +830,21 @@ def main():
             "partition_size": part,
             "host_planned_launch": host_ctx is not None,
         },
+        "value_bytes": "north_star formula: sum ctx x H x D x 2 x 2 B + 4 B per block in use",
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_bytes_per_call": decode_bytes,
-        "timed_call_bytes": call_bytes,
-        "decode_ms_mean": round(dec_mean, 5),
+        "new_rows_bytes_per_step": new_rows_bytes,
+        "fused_ms_mean": round(dec_mean, 5),
+        "fused_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_ms, [10, 50, 90])],
+        "pa_decode_only": {
+            "ms_mean": round(plain_mean, 5),
+            "ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(plain_ms, [10, 50, 90])],
+            "GBps": round(decode_bytes / (plain_mean * 1e-3) / 1e9, 2),
+            "frac": round(decode_bytes / (plain_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "what": "pa_decode alone (no new-row store), HIP events around each call"},
         "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
-        "graph_replay_GBps": None if graph_ms is None else round(step_bytes / (graph_ms * 1e-3) / 1e9, 1),
-        "decode_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(dec_ms, [10, 50, 90])],
+        "graph_replay_GBps": None if graph_ms is None else round(decode_bytes / (graph_ms * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -696,9 +853,142 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "kernel": kernel,
+            "from": "formula bytes / mean HIP-event span of each fused launch (second pass); "
+                    "the rocprofv3 kernel-trace average under profiles/ is the same "
+                    "kernel without the event spans",
         },
+        "reference_reads": refs,
+        "decode_vs_gather": None if refs is None else round(achieved / refs["gather_GBps"], 4),
         "cpu_baseline": cpu,
         "parity_layer0_vs_oracle": parity,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def bench_cow(args):
+    """The shared-prefix / copy-on-write step: 32 prompts of U[64, 512]
+    tokens x 6 samples sharing the prompt's blocks, private tails of
+    U[1, 256] tokens; the step copies the partial last prompt block for 5
+    samples of each prompt (pa_copy_blocks), stores every sample's newest
+    token (pa_write_kv) and decodes every sample (pa_decode), 40 heads x 128,
+    fp16, B = 16, 8 layer pools rotated.  Reports each call's time, the
+    combined step (and the fused form: copies, then pa_decode_append), and
+    the decode's rate over logical bytes (every sample's context, shared
+    blocks counted per sample: the benchmark spec's formula) and over unique bytes
+    (each physical block once)."""
+    import torch
+
+    import paged_kv_cache_05_amd as pa
+    import workloads as W
+
+    device = torch.device("cuda:0")
+    wl = W.shared_prompts(host=False)
+    N, H, D, B = wl.num_seqs, wl.num_heads, wl.head_dim, wl.block_size
+    L, K = args.layers, args.steps
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    pools = [W.device_pools(wl, device, seed_offset=layer) for layer in range(L)]
+    # Every step re-copies the shared partial prompt blocks over the samples'
+    # private copies, which also hold tail tokens: fill the source blocks in
+    # every row (finite values) so that the copies stay finite.
+    src = torch.as_tensor(np.unique(wl.block_mapping[:, 0]), device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(44)
+    for k, v in pools:
+        for pool in (k, v):
+            pool[src] = torch.randn((len(src),) + tuple(pool.shape[1:]), generator=gen,
+                                    device=device).to(pool.dtype)
+    tables, ctx, q = dev(wl.block_tables), dev(wl.context_lens), dev(wl.q)
+    out = torch.empty_like(q)
+    # each sample's newest token: position ctx - 1
+    last = wl.context_lens.astype(np.int64) - 1
+    slots_np = (wl.block_tables[np.arange(N), last // B].astype(np.int64) * B + last % B)
+    slots = dev(slots_np)
+    rng = np.random.default_rng(4)
+    new_k = dev(rng.standard_normal((N, H, D), dtype=np.float32).astype(np.float16))
+    new_v = dev(rng.standard_normal((N, H, D), dtype=np.float32).astype(np.float16))
+    pairs = dev(wl.block_mapping)
+    maxctx = wl.max_context_len
+    ws = pa.new_workspace(N, H, D, maxctx, 256, device=device)
+    scale = float(wl.scale)
+    host_ctx = wl.context_lens
+    stream = torch.cuda.current_stream()
+
+    calls = {
+        "copy": lambda k, v: pa.pa_copy_blocks(k, v, pairs),
+        "write": lambda k, v: pa.pa_write_kv(new_k, new_v, k, v, slots),
+        "decode": lambda k, v: pa.pa_decode(out, q, k, v, tables, ctx, scale, maxctx, 0, ws,
+                                            host_context_lens=host_ctx),
+        "append": lambda k, v: pa.pa_decode_append(out, q, new_k, new_v, k, v, tables, ctx,
+                                                   slots, scale, maxctx, 0, ws,
+                                                   host_context_lens=host_ctx),
+    }
+
+    def timed(names, n):
+        """Mean ms of the listed calls run back to back per step (events
+        around the group), over n steps rotating the layer pools."""
+        for i in range(max(args.warmup, 1)):
+            for nm in names:
+                calls[nm](*pools[i % L])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            for nm in names:
+                calls[nm](*pools[i % L])
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    ms = {nm: timed([nm], K) for nm in ("copy", "write", "decode")}
+    ms["step_split"] = timed(["copy", "write", "decode"], K)
+    ms["step_fused"] = timed(["copy", "append"], K)
+    # the timed region of the line: exactly K fused steps, events at its ends
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(K):
+        calls["copy"](*pools[i % L])
+        calls["append"](*pools[i % L])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    got = out.cpu().numpy()
+    if not np.isfinite(got.astype(np.float32)).all():
+        raise SystemExit("bench: non-finite decode output (shared prefix)")
+
+    logical = wl.algorithmic_bytes()
+    ids, filled = W.live_rows(wl)
+    blocks_used = int(np.sum(-(-wl.context_lens.astype(np.int64) // B)))
+    unique = int(filled.sum()) * H * D * 2 * 2 + 4 * blocks_used
+    npairs = int(wl.block_mapping.shape[0])
+    copy_bytes = npairs * 4 * H * B * D * 2          # read and write, K and V
+    write_bytes = N * H * D * 2 * 4                  # read key/value, write both pools
+    rate = lambda nbytes, m: round(nbytes / (m * 1e-3) / 1e9, 1)
+    rec = {
+        "metric": "shared-prefix decode step: HBM GB/s over logical bytes (north_star formula)",
+        "value": rate(logical, ms_per_step), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded prompt and tail lengths, N(0,1) q/K/V, scattered blocks)",
+        "config": {"workload": "shared-prefix / copy-on-write decode step (32 prompts x 6 "
+                               "samples, 40 heads x 128, B 16)",
+                   "num_seqs": N, "cow_pairs": npairs, "layer_pools_rotated": L,
+                   "sum_context_logical": int(wl.context_lens.sum()),
+                   "unique_tokens": int(filled.sum()), "unique_blocks": int(len(ids))},
+        "logical_bytes": logical, "unique_bytes": unique,
+        "step": "copies (pa_copy_blocks) then pa_decode_append, one layer",
+        "pa_copy_blocks": {"us": round(ms["copy"] * 1e3, 2), "pairs": npairs,
+                           "bytes": copy_bytes, "GBps": rate(copy_bytes, ms["copy"])},
+        "pa_write_kv": {"us": round(ms["write"] * 1e3, 2), "tokens": N,
+                        "bytes": write_bytes, "GBps": rate(write_bytes, ms["write"])},
+        "pa_decode": {"us": round(ms["decode"] * 1e3, 2),
+                      "logical_GBps": rate(logical, ms["decode"]),
+                      "unique_GBps": rate(unique, ms["decode"])},
+        "step_split_us": round(ms["step_split"] * 1e3, 2),
+        "step_fused_us": round(ms["step_fused"] * 1e3, 2),
+        "step_fused_unique_GBps": rate(unique, ms["step_fused"]),
+        "timing": "HIP events around each call (or group), mean over steps",
     }
     print(json.dumps(rec), flush=True)
     return 0

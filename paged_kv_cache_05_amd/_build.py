@@ -1,4 +1,6 @@
-"""Build libpa.so (the C ABI in include/pa.h) with hipcc for gfx950.
+"""Build libpa.so (the C ABI in include/pa.h and include/pa_manager.h) and
+libpa_bench.so (the reference read kernels of include/pa_bench.h, used by
+the benchmark only) with hipcc for gfx950.
 
 Run as ``python -m paged_kv_cache_05_amd._build``; ``__graft_entry__.build()``
 calls :func:`build`.  The library is built in-tree, next to this file.
@@ -16,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_cache.hip", "pa_plan.cpp",
            "pa_manager.cpp"]
 LIBRARY = os.path.join(HERE, "libpa.so")
+BENCH_SOURCES = ["pa_bench.hip"]
+BENCH_LIBRARY = os.path.join(HERE, "libpa_bench.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.  MFMA results
@@ -55,7 +59,8 @@ def _compile(library: str, sources, verbose: bool) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile libpa.so; returns its path."""
+    """Compile both libraries; returns the path of libpa.so."""
+    _compile(BENCH_LIBRARY, BENCH_SOURCES, verbose)
     return _compile(LIBRARY, SOURCES, verbose)
 
 
