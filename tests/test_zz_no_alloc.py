@@ -133,3 +133,42 @@ def test_noalloc_refuses_batches_beyond_the_scratch(pa, device):
     assert "static scratch holds" in pa.pa_last_error()
     torch.cuda.synchronize()
     assert bool((out == 3.0).all().item())
+
+
+def test_noalloc_replayed_from_a_hip_graph(pa, oracle_lib, device):
+    """The callers it is for: pa_decode_noalloc captured into a HIP graph
+    (no allocation inside the capture) and replayed three times, with eager
+    work and synchronisation between replays; every replay reproduces the
+    eager output bit for bit.  The batch spans several partitions, so the
+    static scratch carries the partial results."""
+    wl = W.make("opt13b", num_seqs=24, num_heads=8)
+    k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
+    q, tables, ctx = dev(wl.q, device), dev(wl.block_tables, device), dev(wl.context_lens, device)
+    out = torch.full_like(q, float("nan"))
+
+    def call():
+        pa.pa_decode_noalloc(out, q, k, v, tables, ctx, float(wl.scale), wl.max_context_len,
+                             partition_size=64)
+
+    announce("noalloc eager call before capture")
+    call()
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy()
+    ref = oracle_lib.decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.context_lens, wl.scale)
+    assert close(eager, ref, wl.dtype)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    announce("noalloc capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))               # eager work between replays
+        torch.cuda.synchronize()
+        announce(f"noalloc replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out.cpu().numpy()), bits(eager)), f"replay {r} differs"
