@@ -760,7 +760,7 @@ def bench_decode(args):
         graph_ms = ga.elapsed_time(gb) / (reps * L)
         del g
 
-    # the benchmark spec's byte count: every context token's K and V row for every
+    # The headline byte count: every context token's K and V row for every
     # head, plus one 4-byte table entry per block in use.  The step also
     # stores each sequence's new K/V rows once (reported, not credited).
     decode_bytes = wl.algorithmic_bytes()
@@ -837,7 +837,7 @@ def bench_decode(args):
             "partition_size": part,
             "host_planned_launch": host_ctx is not None,
         },
-        "value_bytes": "north_star formula: sum ctx x H x D x 2 x 2 B + 4 B per block in use",
+        "value_bytes": "sum ctx x H x D x 2 x 2 B + 4 B per block in use",
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_bytes_per_call": decode_bytes,
@@ -885,7 +885,7 @@ def bench_cow(args):
     fp16, B = 16, 8 layer pools rotated.  Reports each call's time, the
     combined step (and the fused form: copies, then pa_decode_append), and
     the decode's rate over logical bytes (every sample's context, shared
-    blocks counted per sample: the benchmark spec's formula) and over unique bytes
+    blocks counted per sample, as in the headline byte count) and over unique bytes
     (each physical block once)."""
     import torch
 
@@ -976,7 +976,7 @@ def bench_cow(args):
     write_bytes = N * H * D * 2 * 4                  # read key/value, write both pools
     rate = lambda nbytes, m: round(nbytes / (m * 1e-3) / 1e9, 1)
     rec = {
-        "metric": "shared-prefix decode step: HBM GB/s over logical bytes (north_star formula)",
+        "metric": "shared-prefix decode step: HBM GB/s over logical bytes (every sample's context)",
         "value": rate(logical, ms_per_step), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",

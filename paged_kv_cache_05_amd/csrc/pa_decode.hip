@@ -104,8 +104,9 @@ __device__ __forceinline__ Chunk load_chunk(const char *p) {
   return c;
 }
 
-// K/V rows are read exactly once per call: non-temporal loads keep them from
-// displacing reusable lines (block tables, q) in the caches.
+// K/V rows that only one workgroup reads are streamed with non-temporal
+// loads, which keep them from displacing reusable lines (block tables, q,
+// shared blocks) in the caches.
 __device__ __forceinline__ Chunk load_stream(const char *p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -115,6 +116,14 @@ __device__ __forceinline__ Chunk load_stream(const char *p) {
   c.w[2] = x.z;
   c.w[3] = x.w;
   return c;
+}
+
+// K/V load of one 16-byte chunk: streamed (non-temporal), or with the
+// default policy that keeps the line in the caches for another reader.
+template <bool kKeep>
+__device__ __forceinline__ Chunk load_kv(const char *p) {
+  if constexpr (kKeep) return load_chunk(p);
+  else return load_stream(p);
 }
 
 __device__ __forceinline__ float dot_chunk(const Chunk &q, const Chunk &k, float acc, _Float16) {
@@ -177,7 +186,7 @@ struct ItemShared {
 // Called by every thread of the workgroup (it synchronises inside).  Writes
 // the output row when the row has a single partition, else this partition's
 // (max, sum, unnormalised output) for the merge pass.
-template <typename T, int D, int B, int W>
+template <typename T, int D, int B, int W, bool kKeep>
 __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T, D, W> &sh,
                                              int b, int h, int part, int ctx, bool append) {
   using G = Geometry<T, D>;
@@ -261,8 +270,8 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
             ka = nk + (col + k * kLPT) * 16;
             va = nv + (col + k * kLPT) * 16;
           }
-          tile.k[g][k] = load_stream(ka);
-          tile.v[g][k] = load_stream(va);
+          tile.k[g][k] = load_kv<kKeep>(ka);
+          tile.v[g][k] = load_kv<kKeep>(va);
         }
       } else {
 #pragma unroll
@@ -542,7 +551,23 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
     return;
   }
   if (part * p.partition_size >= ctx) return;
-  process_item<T, D, B, W>(p, sh, b, h, part, ctx, append);
+  // A partition whose first block the next sequence of the batch maps at the
+  // same logical index is read again by that sequence's workgroups: parallel
+  // samples share their prompt's blocks and sit next to each other in the
+  // batch, and with the head as the grid's fastest index their workgroups for
+  // one head run on the same XCD.  Such an item loads its K/V with the
+  // default, cache-retaining policy; every other item streams them
+  // non-temporally.  The next row's entry is only compared, never used as an
+  // address (the index is below max_blocks_per_seq).  The two entries are
+  // read after the early returns: issued beside the context length they
+  // cost three VGPRs, which at B = 8 would lose the fifth wave per SIMD.
+  const int lb0 = part * p.partition_size / B;
+  const ConstI32 *row_s =
+      (const ConstI32 *)(p.block_tables + (size_t)b * p.max_blocks_per_seq);
+  if (b + 1 < p.num_seqs && row_s[p.max_blocks_per_seq + lb0] == row_s[lb0])
+    process_item<T, D, B, W, true>(p, sh, b, h, part, ctx, append);
+  else
+    process_item<T, D, B, W, false>(p, sh, b, h, part, ctx, append);
 }
 
 // One workgroup per (head, sequence, partition); the hardware dispatcher
