@@ -117,32 +117,50 @@ __device__ inline half8 load_half8(const _Float16 *p) {
   return *reinterpret_cast<const half8 *>(p);
 }
 
-// Per-lane byte offsets, fixed for the whole loop.
+// Per-lane byte offsets, fixed for the whole loop.  Only the first offset
+// of each family is kept; the others differ from it in bits the swizzle
+// owns alone, so one XOR with a constant gives them (no carries: the
+// remaining terms are multiples of 256 bytes):
+//   staging load j:   K at gk ^ (j << 6) (the rows of load j are 4 further
+//                     on at D = 128, which flips bit 2 of swz_k; D = 64 has
+//                     one load), V at gv (swz_v reads row bits 0..1 only);
+//   K operand step j: rk ^ (j << 4) (j covers the chunk bits swz_k flips);
+//   V^T block dt:     rv ^ (dt << 6) (dt covers chunk bits 2..3).
 template <int D>
 struct Offsets {
-  uint32_t gk[Geo<D>::kLoads], gv[Geo<D>::kLoads];   // staging, inside a block
-  uint32_t rk[D / 16];                               // K operand, per head-dim step
-  uint32_t rv[D / 32];                               // V^T operand, per 32 head dims
+  uint32_t gk, gv;   // staging, inside a block
+  uint32_t rk;       // K operand, head-dim step 0
+  uint32_t rv;       // V^T operand, head dims 0..31
 };
 
-template <int D, int B>
-__device__ inline Offsets<D> make_offsets(int h, int w, int lane) {
+template <int D>
+__device__ __forceinline__ uint32_t off_gk(const Offsets<D> &o, int j) {
+  return o.gk ^ (uint32_t)(j << 6);
+}
+template <int D>
+__device__ __forceinline__ uint32_t off_rk(const Offsets<D> &o, int j) {
+  return o.rk ^ (uint32_t)(j << 4);
+}
+template <int D>
+__device__ __forceinline__ uint32_t off_rv(const Offsets<D> &o, int dt) {
+  return o.rv ^ (uint32_t)(dt << 6);
+}
+
+// Staging offsets are relative to the head's rows in a block; the head's
+// offset is added to the (uniform) block base.
+template <int D>
+__device__ inline Offsets<D> make_offsets(int w, int lane) {
   using G = Geo<D>;
+  static_assert(G::kLoads <= 2, "staging offsets of loads past the second");
   Offsets<D> o;
-  const uint32_t head_bytes = (uint32_t)h * B * D * 2;
   const int pos = lane % G::kChunks, sub = lane / G::kChunks;
-#pragma unroll
-  for (int j = 0; j < G::kLoads; ++j) {
-    const int r = w * G::kWaveRows + j * G::kLoadRows + sub;   // tile row this lane fills
-    o.gk[j] = head_bytes + sub * G::kRowBytes + ((pos ^ swz_k<D>(r)) * 16);
-    o.gv[j] = head_bytes + sub * G::kRowBytes + ((pos ^ swz_v<D>(r)) * 16);
-  }
+  const int r = w * G::kWaveRows + sub;   // tile row this lane fills in load 0
+  o.gk = sub * G::kRowBytes + ((pos ^ swz_k<D>(r)) * 16);
+  o.gv = sub * G::kRowBytes + ((pos ^ swz_v<D>(r)) * 16);
   // K operand: lane (c, g) reads row c (plus 32 per key block; the swizzle
   // repeats every 32 rows), chunk g D/16 + j at step j.
   const int c = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j)
-    o.rk[j] = c * G::kRowBytes + (((g * (D / 16) + j) ^ swz_k<D>(c)) * 16);
+  o.rk = c * G::kRowBytes + (((g * (D / 16)) ^ swz_k<D>(c)) * 16);
   // V^T operand by ds_read_b64_tr_b16: in each 16-lane group, result lane
   // i gets element i % 4 of the 4 values read by lanes i / 4, 4 + i / 4,
   // 8 + i / 4 and 12 + i / 4.  So source lane s of group grp reads key row
@@ -154,9 +172,7 @@ __device__ inline Offsets<D> make_offsets(int h, int w, int lane) {
   const int s = lane & 15, grp = lane >> 4;
   const int row = 4 * (grp >> 1) + (s >> 2);
   const int q = 2 * (grp & 1) + ((s & 3) >> 1);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-    o.rv[dt] = row * G::kRowBytes + (((dt * 4 + q) ^ swz_v<D>(row)) * 16) + (s & 1) * 8;
+  o.rv = row * G::kRowBytes + ((q ^ swz_v<D>(row)) * 16) + (s & 1) * 8;
   return o;
 }
 
@@ -173,6 +189,7 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
   const char *kp = static_cast<const char *>(p.k_pool);
   const char *vp = static_cast<const char *>(p.v_pool);
   const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
+  const uint64_t head_bytes = (uint64_t)h * B * D * 2;
   bool fast = key0 + G::kWaveRows <= kv_end;
   int32_t phys[kEnt];
   if (fast) {
@@ -192,17 +209,16 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
       // aligned rows
       const int rj = r0 + j * G::kLoadRows;
       const int e = B >= G::kWaveRows ? 0 : (j * G::kLoadRows) / B;
-      const uint64_t base =
-          (uint64_t)(uint32_t)phys[e] * block_bytes + (uint64_t)((t0 + rj) % B) * G::kRowBytes;
-      __builtin_amdgcn_global_load_lds(kp + base + o.gk[j], st + rj * G::kRowBytes, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + base + o.gv[j],
+      const uint64_t base = (uint64_t)(uint32_t)phys[e] * block_bytes + head_bytes +
+                            (uint64_t)((t0 + rj) % B) * G::kRowBytes;
+      __builtin_amdgcn_global_load_lds(kp + base + off_gk(o, j), st + rj * G::kRowBytes, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + base + o.gv,
                                        st + G::kTensorBytes + rj * G::kRowBytes, 16, 0, 0);
     }
     return;
   }
   // Checked fetch: per lane, the same row and chunk as the direct load.
   const int pos = lane % G::kChunks, sub = lane / G::kChunks;
-  const uint64_t head_bytes = (uint64_t)h * B * D * 2;
 #pragma unroll
   for (int j = 0; j < G::kLoads; ++j) {
     const int rj = r0 + j * G::kLoadRows;
@@ -225,56 +241,214 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
   }
 }
 
-template <int D, int B>
+// One work item: head h, sequence b, query tile qt.
+struct Item {
+  int h, b, qt;
+  int q0, m, n;        // first query row, query tokens and context of the sequence
+  bool empty;          // the tile holds no query of the sequence
+  bool bad;            // inconsistent lengths: the tile's rows get NaN
+  int kv_end;          // keys the tile needs: 0 .. kv_end - 1
+  const int32_t *table;
+};
+
+__device__ __forceinline__ Item make_item(const PrefillParams &p, int h, int b, int qt) {
+  Item it;
+  it.h = h;
+  it.b = b;
+  it.qt = qt;
+  // uniform across the workgroup: kept in scalar registers, so that the
+  // tile loop and the branches on these lengths stay uniform
+  it.q0 = __builtin_amdgcn_readfirstlane(p.query_start[b]);
+  it.m = __builtin_amdgcn_readfirstlane(p.query_start[b + 1]) - it.q0;
+  it.n = min(max(__builtin_amdgcn_readfirstlane(p.context_lens[b]), 0), p.max_context_len);
+  it.empty = qt * kQTile >= it.m;
+  it.bad = it.m < 0 || it.m > it.n || it.q0 < 0 || it.q0 + it.m > p.num_query_rows;
+  const int last = min(it.m, (qt + 1) * kQTile) - 1;
+  it.kv_end = (it.empty || it.bad) ? 0 : it.n - it.m + last + 1;
+  it.table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+  return it;
+}
+
+// The wave's view of an item: lane c of wave w holds query r of the tile,
+// at position pos = n - m + r of the sequence (only pos is kept; r follows).
+struct WaveRows {
+  int pos;           // per lane
+  int wave_pos0;     // the wave's first query position
+  bool active;       // the wave holds a query of the chunk
+  int wave_last;     // the wave's last query position
+};
+
+__device__ __forceinline__ WaveRows wave_rows(const Item &it, int w, int c) {
+  WaveRows v;
+  v.pos = it.n - it.m + it.qt * kQTile + w * kRows + c;
+  v.wave_pos0 = it.n - it.m + it.qt * kQTile + w * kRows;
+  v.active = it.qt * kQTile + w * kRows < it.m && !it.bad;
+  v.wave_last = it.n - it.m + min(it.m, it.qt * kQTile + (w + 1) * kRows) - 1;
+  return v;
+}
+
+// The lane's query index in the sequence's chunk.
+__device__ __forceinline__ int query_row(const Item &it, const WaveRows &v) {
+  return v.pos - (it.n - it.m);
+}
+
+// The query fragments of lane (c, g): head-dim half g of query r.
+template <int D>
+__device__ __forceinline__ void load_q(const PrefillParams &p, const Item &it, const WaveRows &v,
+                                       int g, half8 (&qb)[D / 16]) {
+  const int r = query_row(it, v);
+  const bool q_ok = r < it.m && !it.bad;
+  const _Float16 *row = static_cast<const _Float16 *>(p.q) +
+                        ((int64_t)(it.q0 + r) * p.num_heads + it.h) * D + g * (D / 2);
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) qb[j] = q_ok ? load_half8(row + 8 * j) : half8{};
+}
+
+// The wave's products on one staged tile (keys t0 .. t0 + 31): scores, the
+// online softmax update and the output accumulation.
+template <int D>
+__device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_char *ks,
+                                              const Offsets<D> &o, const half8 (&qb)[D / 16],
+                                              float16v (&acc_o)[D / 32], float &m_run,
+                                              float &l_run, int t0, const WaveRows &v, int g) {
+  using G = Geo<D>;
+  constexpr int kSteps = D / 16;
+  const lds_char *vs = ks + G::kTensorBytes;
+  // S^T = K Q^T per 32-key block.
+  float16v s[kKeyBlocks];
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb) {
+    s[kb] = float16v{};
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const half8 a =
+          *reinterpret_cast<const lds_half8 *>(ks + off_rk(o, j) + kb * 32 * G::kRowBytes);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[j], s[kb], 0, 0, 0);
+    }
+  }
+  // Online softmax for this lane's query over the tile's visible keys.
+  // The maximum is taken on raw scores (the scale is positive) and the
+  // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
+  // Tiles wholly at or below every query of the wave skip the mask.
+  if (t0 + kKeys - 1 > v.wave_pos0) {
+#pragma unroll
+    for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + 32 * kb + (i / 4) * 8 + g * 4 + (i % 4);
+        if (key > v.pos) s[kb][i] = -INFINITY;
+      }
+  }
+  float tile_max = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[kb][i]);
+  tile_max = half_max(tile_max) * p.scale_log2;
+  // Lazy rescaling: the reference m_run moves only when this tile's max
+  // exceeds it by more than kSlack (log2 units); otherwise the weights
+  // of the tile are at most 2^kSlack, well inside fp16 and fp32.
+  // Numerator and denominator share the reference, so the result is the
+  // same softmax; the output is rescaled only when some query's
+  // reference moves.
+  const bool bump = tile_max > m_run + kSlack;
+  const float m_new = bump ? tile_max : m_run;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+  half8 pb[kKeyBlocks][2];
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pb[kb][i / 8][i % 8] =
+          (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -m_use));
+  // The denominator sums the fp16 weights the second product uses.
+  float psum = 0.f;
+  const half2v one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      psum = __builtin_amdgcn_fdot2(
+          half2v{pb[kb][i / 4][2 * (i % 4)], pb[kb][i / 4][2 * (i % 4) + 1]}, one, psum, false);
+  psum = half_sum(psum);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+
+  if (__ballot(bump)) {   // some query's reference moved
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
+  }
+  // O^T += V^T P^T.  k-step kk covers keys 16 kk .. 16 kk + 15 in the
+  // order the score registers hold them: slots 0..3 -> keys
+  // 16 kk + 4 g + e, slots 4..7 -> keys 16 kk + 8 + 4 g + (e - 4).
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int kk = 0; kk < kKeys / 16; ++kk) {
+      const lds_char *vrow = vs + off_rv(o, dt) + 16 * kk * G::kRowBytes;
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)vrow);
+      const short4v hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(vrow + 8 * G::kRowBytes));
+      const half8 a = __builtin_bit_cast(
+          half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk / 2][kk % 2], acc_o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// The tile's output rows (rows in range only).  Lane holds O^T[d][query c]
+// for d = 32 dt + 8 (i/4) + 4 g + (i%4).
+template <int D>
+__device__ __forceinline__ void store_rows(const PrefillParams &p, const Item &it,
+                                           const WaveRows &v, int g,
+                                           const float16v (&acc_o)[D / 32], float l_run) {
+  const int r = query_row(it, v);
+  if (r >= it.m || it.q0 + r >= p.num_query_rows || it.q0 + r < 0) return;
+  const float inv = (it.bad || !(l_run > 0.f)) ? NAN : 1.f / l_run;
+  _Float16 *orow =
+      static_cast<_Float16 *>(p.out) + ((int64_t)(it.q0 + r) * p.num_heads + it.h) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      half4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(acc_o[dt][i4 * 4 + e] * inv);
+      *reinterpret_cast<half4 *>(orow + dt * 32 + i4 * 8 + g * 4) = o4;
+    }
+}
+
 // With nchunks > 1 the workgroup covers key chunk `chunk` of the tile's
 // keys (an equal share of its 32-key tiles) and writes that chunk's partial
 // result to slot `slot` for the merge pass.
-__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds,
-                             int chunk = 0, int nchunks = 1, int slot = 0) {
-  using G = Geo<D>;
-  const int q0 = p.query_start[b];
-  const int m = p.query_start[b + 1] - q0;
-  const int n = min(max(p.context_lens[b], 0), p.max_context_len);
-  if (qt * kQTile >= m) return;
-  const bool bad_seq = m < 0 || m > n || q0 < 0 || q0 + m > p.num_query_rows;
-
+template <int D, int B>
+__device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds0,
+                             lds_char *lds1, int chunk = 0, int nchunks = 1, int slot = 0) {
+  const Item it = make_item(p, h, b, qt);
+  if (it.empty) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 31;                 // this lane's query column / key row
   const int g = lane >> 5;                 // lane group
-  const int r = qt * kQTile + w * kRows + c;         // query index in the chunk
-  const bool q_ok = r < m && !bad_seq;
-  const int pos = n - m + r;                         // its position in the sequence
-  const int last = min(m, (qt + 1) * kQTile) - 1;
-  const int kv_end = bad_seq ? 0 : n - m + last + 1; // keys the workgroup needs
-  const int wave_pos0 = n - m + qt * kQTile + w * kRows;   // the wave's first query position
   // The wave's products are skipped when it holds no query of the chunk,
   // and for key tiles past its last query (it still stages its rows and
   // meets every barrier).
-  const bool wave_active = qt * kQTile + w * kRows < m && !bad_seq;
-  const int wave_last = n - m + min(m, qt * kQTile + (w + 1) * kRows) - 1;
-  const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-  const Offsets<D> o = make_offsets<D, B>(h, w, lane);
+  const WaveRows v = wave_rows(it, w, c);
+  const Offsets<D> o = make_offsets<D>(w, lane);
 
-  constexpr int kSteps = D / 16;
-  half8 qb[kSteps];
-  {
-    const _Float16 *row = static_cast<const _Float16 *>(p.q) +
-                          ((int64_t)(q0 + r) * p.num_heads + h) * D + g * (D / 2);
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) qb[j] = q_ok ? load_half8(row + 8 * j) : half8{};
-  }
-
+  half8 qb[D / 16];
+  load_q<D>(p, it, v, g, qb);
   float16v acc_o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
   float m_run = -INFINITY, l_run = 0.f;
 
   // This workgroup's keys [k_lo, k_hi): all of them, or one chunk.
-  const int ntiles = (kv_end + kKeys - 1) / kKeys;
+  const int ntiles = (it.kv_end + kKeys - 1) / kKeys;
   const int k_lo = (int)((int64_t)ntiles * chunk / nchunks) * kKeys;
-  const int k_hi = min(kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
-  if (k_lo < k_hi) stage_rows<D, B>(p, table, h, w, lane, kv_end, k_lo, lds, o);
+  const int k_hi = min(it.kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
+  if (k_lo < k_hi) stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o);
   __builtin_amdgcn_s_waitcnt(0);   // query fragments and the first tile
   __syncthreads();
 
@@ -284,93 +458,10 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   // immediate.
   auto step = [&](auto stage, int t0) {
     constexpr int kS = decltype(stage)::value;
-    lds_char *cur = lds + kS * G::kStageBytes;
+    lds_char *cur = kS ? lds1 : lds0;
     if (t0 + kKeys < k_hi)
-      stage_rows<D, B>(p, table, h, w, lane, kv_end, t0 + kKeys, lds + (kS ^ 1) * G::kStageBytes, o);
-    if (wave_active && t0 <= wave_last) {
-      const lds_char *ks = cur;
-      const lds_char *vs = cur + G::kTensorBytes;
-      // S^T = K Q^T per 32-key block.
-      float16v s[kKeyBlocks];
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb) {
-        s[kb] = float16v{};
-#pragma unroll
-        for (int j = 0; j < kSteps; ++j) {
-          const half8 a = *reinterpret_cast<const lds_half8 *>(ks + o.rk[j] + kb * 32 * G::kRowBytes);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[j], s[kb], 0, 0, 0);
-        }
-      }
-      // Online softmax for this lane's query over the tile's visible keys.
-      // The maximum is taken on raw scores (the scale is positive) and the
-      // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
-      // Tiles wholly at or below every query of the wave skip the mask.
-      if (t0 + kKeys - 1 > wave_pos0) {
-#pragma unroll
-        for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = t0 + 32 * kb + (i / 4) * 8 + g * 4 + (i % 4);
-            if (key > pos) s[kb][i] = -INFINITY;
-          }
-      }
-      float tile_max = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[kb][i]);
-      tile_max = half_max(tile_max) * p.scale_log2;
-      // Lazy rescaling: the reference m_run moves only when this tile's max
-      // exceeds it by more than kSlack (log2 units); otherwise the weights
-      // of the tile are at most 2^kSlack, well inside fp16 and fp32.
-      // Numerator and denominator share the reference, so the result is the
-      // same softmax; the output is rescaled only when some query's
-      // reference moves.
-      const bool bump = tile_max > m_run + kSlack;
-      const float m_new = bump ? tile_max : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-      half8 pb[kKeyBlocks][2];
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          pb[kb][i / 8][i % 8] =
-              (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -m_use));
-      // The denominator sums the fp16 weights the second product uses.
-      float psum = 0.f;
-      const half2v one = {(_Float16)1.f, (_Float16)1.f};
-#pragma unroll
-      for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          psum = __builtin_amdgcn_fdot2(
-              half2v{pb[kb][i / 4][2 * (i % 4)], pb[kb][i / 4][2 * (i % 4) + 1]}, one, psum, false);
-      psum = half_sum(psum);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-
-      if (__ballot(bump)) {   // some query's reference moved
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
-      }
-      // O^T += V^T P^T.  k-step kk covers keys 16 kk .. 16 kk + 15 in the
-      // order the score registers hold them: slots 0..3 -> keys
-      // 16 kk + 4 g + e, slots 4..7 -> keys 16 kk + 8 + 4 g + (e - 4).
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int kk = 0; kk < kKeys / 16; ++kk) {
-          const lds_char *vrow = vs + o.rv[dt] + 16 * kk * G::kRowBytes;
-          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)vrow);
-          const short4v hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(vrow + 8 * G::kRowBytes));
-          const half8 a = __builtin_bit_cast(
-              half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk / 2][kk % 2], acc_o[dt], 0, 0, 0);
-        }
-      }
-    }
+      stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o);
+    if (v.active && t0 <= v.wave_last) tile_products<D>(p, cur, o, qb, acc_o, m_run, l_run, t0, v, g);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
   };
@@ -380,8 +471,9 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
 
-  if (r >= m || q0 + r >= p.num_query_rows || q0 + r < 0) return;   // rows in range only
   if (nchunks > 1) {
+    const int r = query_row(it, v);
+    if (r >= it.m || it.q0 + r >= p.num_query_rows || it.q0 + r < 0) return;
     // Partial result: the unnormalised output and (m, l) of this chunk,
     // for the merge pass; an empty chunk leaves m = -inf, l = 0, O = 0.
     const size_t prow = ((size_t)slot * p.num_heads + h) * kQTile + w * kRows + c;
@@ -396,18 +488,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     if (g == 0) p.part_ml[prow] = make_float2(m_run, l_run);
     return;
   }
-  // Lane holds O^T[d][query c] for d = 32 dt + 8 (i/4) + 4 g + (i%4).
-  const float inv = (bad_seq || !(l_run > 0.f)) ? NAN : 1.f / l_run;
-  _Float16 *orow = static_cast<_Float16 *>(p.out) + ((int64_t)(q0 + r) * p.num_heads + h) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      half4 o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(acc_o[dt][i4 * 4 + e] * inv);
-      *reinterpret_cast<half4 *>(orow + dt * 32 + i4 * 8 + g * 4) = o4;
-    }
+  store_rows<D>(p, it, v, g, acc_o, l_run);
 }
 
 // Waves per SIMD the register budget is set for (168 VGPRs).  Two stages of
@@ -422,9 +503,10 @@ constexpr int waves_per_eu() {
 template <int D, int B>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
 prefill_kernel(const PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
   prefill_item<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y,
-                     (lds_char *)lds);
+                     (lds_char *)lds0, (lds_char *)lds1);
 }
 
 // grid (heads, items): items = sequence << 16 | query tile, in the order the
@@ -432,19 +514,23 @@ prefill_kernel(const PrefillParams p) {
 template <int D, int B>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
 prefill_listed_kernel(const PrefillParams p, const WorkList items) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
   const uint32_t it = items.item[blockIdx.y];
-  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds);
+  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds0,
+                     (lds_char *)lds1);
 }
 
 // grid (heads, split list entries): one key chunk of one query tile each.
 template <int D, int B>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D>())))
 prefill_split_kernel(const PrefillParams p, const SplitList items) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
   const uint32_t it = items.item[blockIdx.y], part = items.part[blockIdx.y];
-  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds,
-                     (int)((part >> 4) & 15u), (int)(part & 15u) + 1, (int)(part >> 8));
+  prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds0,
+                     (lds_char *)lds1, (int)((part >> 4) & 15u), (int)(part & 15u) + 1,
+                     (int)(part >> 8));
 }
 
 // Merge of a split tile's chunks: grid (heads, split tiles, row groups),
