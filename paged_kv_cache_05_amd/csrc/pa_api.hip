@@ -389,9 +389,13 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
                                  waves, static_cast<hipStream_t>(stream));
       });
   }
+  // Grid launch: 4-wave workgroups when no row is longer than 256 tokens, 8
+  // otherwise (long rows keep the 8-wave form whatever the partition size).
+  constexpr int kGridShortTokens = 256;
+  const int grid_waves = max_context_len <= kGridShortTokens ? 4 : 8;
   return launch_checked(what, [&] {
-    return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr, 8,
-                             static_cast<hipStream_t>(stream));
+    return pa::launch_decode(p, num_seqs, head_dim, block_size, dtype, nullptr, nullptr,
+                             grid_waves, static_cast<hipStream_t>(stream));
   });
 }
 

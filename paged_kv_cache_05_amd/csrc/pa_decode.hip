@@ -646,9 +646,11 @@ __global__ void __launch_bounds__(D) merge_listed_kernel(const DecodeParams p,
   merge_one<T, D>(p, blockIdx.x, (int)rows.item[blockIdx.y]);
 }
 
-// Waves per workgroup of the grid launch: 8 (4 and 16 measured slower on
-// the lognormal batch).  The listed launch also has a 4-wave form for
-// batches of short rows, where 8 waves leave most of them one tile or none.
+// Waves per workgroup: 8 (4 and 16 measured slower on the lognormal batch).
+// Both launches also have a 4-wave form for short rows, where 8 waves leave
+// most of them one tile or none: the listed launch when its items average
+// under 12 tiles, the grid launch when no row is longer than 256 tokens (the
+// host's bound on every row).
 constexpr int kDecodeWaves = 8;
 
 struct Lists {
@@ -677,9 +679,9 @@ hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_
           <<<dim3(p.num_heads, l.merge_rows->count), D, 0, stream>>>(p, *l.merge_rows);
     return hipGetLastError();
   }
-  decode_kernel<T, D, B, W><<<dim3(p.num_heads + (p.new_key != nullptr ? 1 : 0), num_seqs,
-                                   p.num_partitions),
-                              64 * W, 0, stream>>>(p);
+  const dim3 grid(p.num_heads + (p.new_key != nullptr ? 1 : 0), num_seqs, p.num_partitions);
+  if (l.waves == 4) decode_kernel<T, D, B, 4><<<grid, 64 * 4, 0, stream>>>(p);
+  else decode_kernel<T, D, B, W><<<grid, 64 * W, 0, stream>>>(p);
   if (p.num_partitions > 1)
     merge_kernel<T, D><<<dim3(p.num_heads, num_seqs), D, 0, stream>>>(p);
   return hipGetLastError();

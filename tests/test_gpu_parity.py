@@ -351,6 +351,13 @@ def planned_waves(ctx, part, block_size):
     return 8 if items * 12 * 16 <= int(np.sum(ctx)) else 4
 
 
+def grid_waves(wl):
+    """The unplanned grid launch's waves per workgroup: 4 when the bound
+    max_context_len that gpu_decode passes (the longest row) is at most 256
+    tokens, else 8."""
+    return 4 if int(np.max(wl.context_lens)) <= 256 else 8
+
+
 @pytest.mark.parametrize("name,kw,part", [
     ("tiny", {}, 16), ("tiny", {}, 0), ("opt13b", {}, 0), ("opt13b", {}, 256), ("opt13b", {}, 1024), ("short", {"block_size": 8}, 0),
     ("short", {"block_size": 32}, 64), ("cow", {}, 0), ("cow", {}, 128),
@@ -360,15 +367,17 @@ def planned_waves(ctx, part, block_size):
 def test_host_planned_launch(pa, oracle_lib, device, name, kw, part):
     """With host-side context lengths the library launches only the non-empty
     (sequence, partition) items, long ones first.  With an explicit partition
-    size and 8-wave workgroups the results are bit-identical to the unplanned
-    launch (same per-partition reduction order); with partition_size 0 the
-    library also picks the partition size from the lengths."""
+    size and 8-wave workgroups on both sides (the plan keeps 8, and the
+    unplanned grid keeps 8 because some row is longer than 256 tokens) the
+    results are bit-identical to the unplanned launch (same per-partition
+    reduction order); with partition_size 0 the library also picks the
+    partition size from the lengths."""
     wl = workload(name, **kw)
     k, v = dev(wl.k_pool, device), dev(wl.v_pool, device)
     announce(f"{wl.name}: planned vs unplanned, partition {part}")
     plain = gpu_decode(pa, wl, k, v, device, partition_size=part)
     planned = gpu_decode(pa, wl, k, v, device, partition_size=part, host_ctx=wl.context_lens)
-    if part and planned_waves(wl.context_lens, part, wl.block_size) == 8:
+    if part and planned_waves(wl.context_lens, part, wl.block_size) == 8 and grid_waves(wl) == 8:
         assert np.array_equal(bits(planned), bits(plain))
     assert_close(planned, oracle_decode(oracle_lib, wl), wl.dtype, wl.name)
 
