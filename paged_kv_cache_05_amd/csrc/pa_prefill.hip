@@ -102,10 +102,16 @@ __device__ __forceinline__ int swz_v(int r) {
 __device__ inline void swap_halves(unsigned &a, unsigned &b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// The maximum of x over lanes l and l ^ 32, in one block with the swap: a
+// plain v_max_f32 (NaN inputs are ignored, as fmaxf does), without the
+// canonicalising moves the compiler puts on values it did not produce.  The
+// second s_nop covers the VALU read of the swapped registers.
 __device__ inline float half_max(float x) {
   unsigned a = __builtin_bit_cast(unsigned, x), b = a;
-  swap_halves(a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  float r;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %1, %2\n\ts_nop 1\n\tv_max_f32 %0, %1, %2"
+               : "=v"(r), "+v"(a), "+v"(b));
+  return r;
 }
 __device__ inline float half_sum(float x) {
   unsigned a = __builtin_bit_cast(unsigned, x), b = a;
@@ -176,32 +182,47 @@ __device__ inline Offsets<D> make_offsets(int w, int lane) {
   return o;
 }
 
-// Stages this wave's rows [w kWaveRows, (w+1) kWaveRows) of the tile at t0
-// into the stage buffer st (K, then V).
+// The table entries of this wave's rows [w kWaveRows, (w+1) kWaveRows) of
+// the tile at t0, loaded when those rows all precede kv_end (so the entries
+// lie inside the table row).  Uniform: scalar loads.  Nothing here reads the
+// loaded values, so the wait for them falls at their use in stage_rows.
+template <int D, int B>
+struct TileEntries {
+  static constexpr int kEnt = B >= Geo<D>::kWaveRows ? 1 : Geo<D>::kWaveRows / B;
+  int32_t phys[kEnt];
+  bool in_row;
+};
+
+template <int D, int B>
+__device__ inline TileEntries<D, B> tile_entries(const int32_t *table, int w, int kv_end,
+                                                 int t0) {
+  using G = Geo<D>;
+  TileEntries<D, B> e;
+  const int key0 = t0 + w * G::kWaveRows;
+  e.in_row = key0 + G::kWaveRows <= kv_end;
+  const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
+#pragma unroll
+  for (int i = 0; i < TileEntries<D, B>::kEnt; ++i) e.phys[i] = e.in_row ? ctab[key0 / B + i] : 0;
+  return e;
+}
+
+// Stages this wave's rows of the tile at t0 into the stage buffer st (K,
+// then V), given the rows' entries from tile_entries.  Rows whose entries
+// all lie in the pool take direct loads; the others the checked fetch.
 template <int D, int B>
 __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, int h, int w,
                                   int lane, int kv_end, int t0, lds_char *st,
-                                  const Offsets<D> &o) {
+                                  const Offsets<D> &o, const TileEntries<D, B> &ent) {
   using G = Geo<D>;
   const int r0 = w * G::kWaveRows;
-  const int key0 = t0 + r0;
-  constexpr int kEnt = B >= G::kWaveRows ? 1 : G::kWaveRows / B;
   const char *kp = static_cast<const char *>(p.k_pool);
   const char *vp = static_cast<const char *>(p.v_pool);
   const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
   const uint64_t head_bytes = (uint64_t)h * B * D * 2;
-  bool fast = key0 + G::kWaveRows <= kv_end;
-  int32_t phys[kEnt];
-  if (fast) {
-    // uniform entries by scalar loads; the rows all precede kv_end, so the
-    // entries lie inside the table row
-    const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
+  bool fast = ent.in_row;
 #pragma unroll
-    for (int e = 0; e < kEnt; ++e) {
-      phys[e] = ctab[key0 / B + e];
-      fast = fast && phys[e] >= 0 && phys[e] < p.num_blocks;
-    }
-  }
+  for (int i = 0; i < TileEntries<D, B>::kEnt; ++i)
+    fast = fast && ent.phys[i] >= 0 && ent.phys[i] < p.num_blocks;
   if (fast) {
 #pragma unroll
     for (int j = 0; j < G::kLoads; ++j) {
@@ -209,7 +230,7 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
       // aligned rows
       const int rj = r0 + j * G::kLoadRows;
       const int e = B >= G::kWaveRows ? 0 : (j * G::kLoadRows) / B;
-      const uint64_t base = (uint64_t)(uint32_t)phys[e] * block_bytes + head_bytes +
+      const uint64_t base = (uint64_t)(uint32_t)ent.phys[e] * block_bytes + head_bytes +
                             (uint64_t)((t0 + rj) % B) * G::kRowBytes;
       __builtin_amdgcn_global_load_lds(kp + base + off_gk(o, j), st + rj * G::kRowBytes, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vp + base + o.gv,
@@ -330,14 +351,16 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   // The maximum is taken on raw scores (the scale is positive) and the
   // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
   // Tiles wholly at or below every query of the wave skip the mask.
+  // Slot i of key block kb holds key t0 + 32 kb + 8 (i / 4) + 4 g + i % 4;
+  // it is masked when that key lies past the lane's query position, i.e.
+  // when its constant part 32 kb + 8 (i / 4) + i % 4 exceeds pos - t0 - 4 g.
   if (t0 + kKeys - 1 > v.wave_pos0) {
+    const int lim = v.pos - t0 - 4 * g;
 #pragma unroll
     for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = t0 + 32 * kb + (i / 4) * 8 + g * 4 + (i % 4);
-        if (key > v.pos) s[kb][i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (32 * kb + (i / 4) * 8 + (i % 4) > lim) s[kb][i] = -INFINITY;
   }
   float tile_max = -INFINITY;
 #pragma unroll
@@ -354,31 +377,45 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   const bool bump = tile_max > m_run + kSlack;
   const float m_new = bump ? tile_max : m_run;
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-  half8 pb[kKeyBlocks][2];
+  // Weights rounded to fp16 (round to nearest even) two at a time.
+  unsigned pw[kKeyBlocks][8];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pb[kb][i / 8][i % 8] =
-          (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][i], p.scale_log2, -m_use));
-  // The denominator sums the fp16 weights the second product uses.
+    for (int i = 0; i < 8; ++i) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], p.scale_log2, -m_use));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], p.scale_log2, -m_use));
+      asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(pw[kb][i]) : "v"(e0), "v"(e1));
+    }
+  // The denominator sums the fp16 weights the second product uses.  Each
+  // lane sums its own 16 keys of the tile; lanes l and l ^ 32 hold the same
+  // query with the same reference and scale factor, so their sums are added
+  // once, after the loop.
   float psum = 0.f;
   const half2v one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      psum = __builtin_amdgcn_fdot2(
-          half2v{pb[kb][i / 4][2 * (i % 4)], pb[kb][i / 4][2 * (i % 4) + 1]}, one, psum, false);
-  psum = half_sum(psum);
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-
-  if (__ballot(bump)) {   // some query's reference moved
+      psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pw[kb][i]), one, psum, false);
+  if (__ballot(bump)) {   // some query's reference moved: rescale its state
+    const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+    l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
   }
+  l_run += psum;
+  m_run = m_new;
+  half8 pb[kKeyBlocks][2];
+#pragma unroll
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      pb[kb][j] = __builtin_bit_cast(
+          half8, u32x4{pw[kb][4 * j], pw[kb][4 * j + 1], pw[kb][4 * j + 2], pw[kb][4 * j + 3]});
+    }
+
   // O^T += V^T P^T.  k-step kk covers keys 16 kk .. 16 kk + 15 in the
   // order the score registers hold them: slots 0..3 -> keys
   // 16 kk + 4 g + e, slots 4..7 -> keys 16 kk + 8 + 4 g + (e - 4).
@@ -448,7 +485,12 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   const int ntiles = (it.kv_end + kKeys - 1) / kKeys;
   const int k_lo = (int)((int64_t)ntiles * chunk / nchunks) * kKeys;
   const int k_hi = min(it.kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
-  if (k_lo < k_hi) stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o);
+  if (k_lo < k_hi)
+    stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o,
+                     tile_entries<D, B>(it.table, w, it.kv_end, k_lo));
+  // The next tile's entries are loaded one step ahead, so that their wait
+  // falls under the product's LDS waits instead of before the staging.
+  TileEntries<D, B> ent = tile_entries<D, B>(it.table, w, it.kv_end, k_lo + kKeys);
   __builtin_amdgcn_s_waitcnt(0);   // query fragments and the first tile
   __syncthreads();
 
@@ -460,7 +502,8 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     constexpr int kS = decltype(stage)::value;
     lds_char *cur = kS ? lds1 : lds0;
     if (t0 + kKeys < k_hi)
-      stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o);
+      stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o, ent);
+    ent = tile_entries<D, B>(it.table, w, it.kv_end, t0 + 2 * kKeys);
     if (v.active && t0 <= v.wave_last) tile_products<D>(p, cur, o, qb, acc_o, m_run, l_run, t0, v, g);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
@@ -470,6 +513,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     if (t0 + kKeys >= k_hi) break;
     step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
+  l_run = half_sum(l_run);   // the two lanes' partial denominators
 
   if (nchunks > 1) {
     const int r = query_row(it, v);
