@@ -347,6 +347,19 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qb[j], s[kb], 0, 0, 0);
     }
   }
+  // Schedule: the K operand reads run kAhead steps ahead of the score
+  // MFMAs (LDS reads, then one MFMA and one read per step), so that the
+  // reads of later steps return under the earlier MFMAs instead of each
+  // pair waiting for its own.  Three steps ahead keeps every instantiation
+  // within the three-waves-per-SIMD register budget without scratch.
+  constexpr int kAhead = kSteps < 3 ? kSteps : 3;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // LDS reads
+#pragma unroll
+  for (int j = 0; j < kSteps - kAhead; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   // Online softmax for this lane's query over the tile's visible keys.
   // The maximum is taken on raw scores (the scale is positive) and the
   // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
@@ -432,6 +445,15 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
       acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kk / 2][kk % 2], acc_o[dt], 0, 0, 0);
     }
   }
+  // Schedule: the Vᵀ reads of two 32-dim blocks first, then each block's
+  // two MFMAs followed by the reads of the block two ahead.
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);        // LDS reads
+#pragma unroll
+  for (int dt = 0; dt < D / 32 - 2; ++dt) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // The tile's output rows (rows in range only).  Lane holds O^T[d][query c]
