@@ -325,13 +325,22 @@ __device__ __forceinline__ void load_q(const PrefillParams &p, const Item &it, c
   for (int j = 0; j < D / 16; ++j) qb[j] = q_ok ? load_half8(row + 8 * j) : half8{};
 }
 
+// A lane's online-softmax state for its query.  m is the reference the
+// weights are taken against (log2 units, -inf until the query has seen a
+// key), m_use the same but 0 while m is -inf (so that weights of masked
+// keys come out 0, never NaN), thr the raw score above which the reference
+// moves, (m + kSlack) / scale_log2, and l this lane's partial denominator.
+struct SoftmaxState {
+  float m = -INFINITY, m_use = 0.f, thr = -INFINITY, l = 0.f;
+};
+
 // The wave's products on one staged tile (keys t0 .. t0 + 31): scores, the
 // online softmax update and the output accumulation.
 template <int D>
 __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_char *ks,
                                               const Offsets<D> &o, const half8 (&qb)[D / 16],
-                                              float16v (&acc_o)[D / 32], float &m_run,
-                                              float &l_run, int t0, const WaveRows &v, int g) {
+                                              float16v (&acc_o)[D / 32], SoftmaxState &sm,
+                                              int t0, const WaveRows &v, int g) {
   using G = Geo<D>;
   constexpr int kSteps = D / 16;
   const lds_char *vs = ks + G::kTensorBytes;
@@ -380,16 +389,29 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[kb][i]);
-  tile_max = half_max(tile_max) * p.scale_log2;
-  // Lazy rescaling: the reference m_run moves only when this tile's max
-  // exceeds it by more than kSlack (log2 units); otherwise the weights
-  // of the tile are at most 2^kSlack, well inside fp16 and fp32.
-  // Numerator and denominator share the reference, so the result is the
-  // same softmax; the output is rescaled only when some query's
-  // reference moves.
-  const bool bump = tile_max > m_run + kSlack;
-  const float m_new = bump ? tile_max : m_run;
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  tile_max = half_max(tile_max);
+  // Lazy rescaling: the reference moves only when this tile's max exceeds
+  // it by more than kSlack (log2 units); otherwise the weights of the tile
+  // are at most 2^kSlack, well inside fp16 and fp32.  Numerator and
+  // denominator share the reference, so the result is the same softmax.
+  // The test runs on the raw maximum (the scale is positive) against the
+  // threshold kept in raw units; the new reference, the rescaling of the
+  // output and of the denominator happen only when some query's reference
+  // moves.
+  const bool bump = tile_max > sm.thr;
+  if (__ballot(bump)) {
+    const float m_new = tile_max * p.scale_log2;
+    const float alpha = bump ? __builtin_amdgcn_exp2f(sm.m - m_new) : 1.f;
+    sm.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
+    if (bump) {
+      sm.m = m_new;
+      sm.m_use = m_new;
+      sm.thr = (m_new + kSlack) / p.scale_log2;
+    }
+  }
+  const float m_use = sm.m_use;
   // Weights rounded to fp16 (round to nearest even) two at a time.
   unsigned pw[kKeyBlocks][8];
 #pragma unroll
@@ -411,14 +433,7 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pw[kb][i]), one, psum, false);
-  if (__ballot(bump)) {   // some query's reference moved: rescale its state
-    const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] *= alpha;
-  }
-  l_run += psum;
-  m_run = m_new;
+  sm.l += psum;
   half8 pb[kKeyBlocks][2];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
@@ -501,7 +516,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   float16v acc_o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
-  float m_run = -INFINITY, l_run = 0.f;
+  SoftmaxState sm;
 
   // This workgroup's keys [k_lo, k_hi): all of them, or one chunk.
   const int ntiles = (it.kv_end + kKeys - 1) / kKeys;
@@ -526,7 +541,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     if (t0 + kKeys < k_hi)
       stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o, ent);
     ent = tile_entries<D, B>(it.table, w, it.kv_end, t0 + 2 * kKeys);
-    if (v.active && t0 <= v.wave_last) tile_products<D>(p, cur, o, qb, acc_o, m_run, l_run, t0, v, g);
+    if (v.active && t0 <= v.wave_last) tile_products<D>(p, cur, o, qb, acc_o, sm, t0, v, g);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
   };
@@ -535,7 +550,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     if (t0 + kKeys >= k_hi) break;
     step(std::integral_constant<int, 1>{}, t0 + kKeys);
   }
-  l_run = half_sum(l_run);   // the two lanes' partial denominators
+  const float l_run = half_sum(sm.l);   // the two lanes' partial denominators
 
   if (nchunks > 1) {
     const int r = query_row(it, v);
@@ -551,7 +566,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
         *reinterpret_cast<float4 *>(po + dt * 32 + i4 * 8 + g * 4) =
             make_float4(acc_o[dt][i4 * 4], acc_o[dt][i4 * 4 + 1], acc_o[dt][i4 * 4 + 2],
                         acc_o[dt][i4 * 4 + 3]);
-    if (g == 0) p.part_ml[prow] = make_float2(m_run, l_run);
+    if (g == 0) p.part_ml[prow] = make_float2(sm.m, l_run);
     return;
   }
   store_rows<D>(p, it, v, g, acc_o, l_run);
