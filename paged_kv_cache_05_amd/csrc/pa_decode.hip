@@ -181,6 +181,27 @@ struct ItemShared {
   float o[kStates][D];
 };
 
+// Table entries of a wave's first 16-token tile (one per block the tile
+// spans), loaded before the context length is known.
+template <int B>
+struct FirstEntries {
+  static constexpr int kCount = B >= 16 ? 1 : 16 / B;
+  int32_t e[kCount];
+};
+
+// This lane's chunk(s) of the query row (b, h).
+template <typename T, int D>
+__device__ __forceinline__ void load_q(const DecodeParams &p, int b, int h,
+                                       Chunk (&qc)[Geometry<T, D>::kChunksPerLane]) {
+  using G = Geometry<T, D>;
+  const int col = (threadIdx.x & 63) % G::kLanesPerToken;
+  const char *qp =
+      reinterpret_cast<const char *>(p.q) + ((size_t)b * p.num_heads + h) * D * sizeof(T);
+#pragma unroll
+  for (int k = 0; k < G::kChunksPerLane; ++k)
+    qc[k] = load_chunk(qp + (col + k * G::kLanesPerToken) * 16);
+}
+
 // One work item: sequence b, head h, context partition `part` (tokens
 // [part * P, min(ctx, (part + 1) * P)), non-empty), ctx already clamped.
 // Called by every thread of the workgroup (it synchronises inside).  Writes
@@ -188,7 +209,9 @@ struct ItemShared {
 // (max, sum, unnormalised output) for the merge pass.
 template <typename T, int D, int B, int W, bool kKeep>
 __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T, D, W> &sh,
-                                             int b, int h, int part, int ctx, bool append) {
+                                             int b, int h, int part, int ctx, bool append,
+                                             const FirstEntries<B> &first,
+                                             const Chunk (&qc)[Geometry<T, D>::kChunksPerLane]) {
   using G = Geometry<T, D>;
   constexpr int kStates = ItemShared<T, D, W>::kStates;
   constexpr int kLPT = G::kLanesPerToken;
@@ -206,12 +229,6 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
   const int col = lane % kLPT;   // which 16-byte chunk(s) of a token row
   const int trow = lane / kLPT;  // which token of a 4- or 8-token group
 
-  Chunk qc[G::kChunksPerLane];
-  {
-    const char *qp = reinterpret_cast<const char *>(p.q) + row * D * sizeof(T);
-#pragma unroll
-    for (int k = 0; k < G::kChunksPerLane; ++k) qc[k] = load_chunk(qp + (col + k * kLPT) * 16);
-  }
 
   // Two views of the sequence's table row.  Inside the tile loop entries are
   // read through the constant address space: the kernel never writes the
@@ -238,10 +255,13 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
 
   // Load the 16-token tile starting at logical token ts.  With kCheck,
   // groups at or past tok_end are not loaded (their table entries may not
-  // exist); full tiles skip the check.  kScalar picks the table view.
-  auto fetch = [&](Tile<T, D> &tile, int ts, auto check_tag, auto scalar_tag) {
+  // exist); full tiles skip the check.  kScalar picks the table view;
+  // kFirst takes the entries from `first` (the wave's first tile).
+  auto fetch = [&](Tile<T, D> &tile, int ts, auto check_tag, auto scalar_tag,
+                   auto first_tag) {
     constexpr bool kCheck = decltype(check_tag)::value;
     constexpr bool kScalar = decltype(scalar_tag)::value;
+    constexpr bool kFirst = decltype(first_tag)::value;
 #pragma unroll
     for (int g = 0; g < G::kGroups; ++g) {
       const int gs = ts + g * kTPG;
@@ -254,7 +274,8 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
         off = gs % B;
       }
       if (!kCheck || gs < tok_end) {
-        const int phys = kScalar ? table_s[lb] : table[lb];
+        const int phys = kFirst ? first.e[B >= 16 ? 0 : (g * kTPG) / B]
+                                : (kScalar ? table_s[lb] : table[lb]);
         const bool ok = (unsigned)phys < num_blocks;
         bad |= !ok;
         const size_t boff = (size_t)(ok ? phys : 0) * block_bytes + (size_t)off * D * sizeof(T);
@@ -347,18 +368,18 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
     const int iters = nfull > wave ? (nfull - wave + W - 1) / W : 0;
     Tile<T, D> ta, tb;
     auto tile_start = [&](int n) { return tok0 + (wave + n * W) * G::kTile; };
-    if (iters > 0) fetch(ta, tile_start(0), std::false_type(), std::false_type());
+    if (iters > 0) fetch(ta, tile_start(0), std::false_type(), std::false_type(), std::true_type());
     int n = 0;
     for (; n + 2 < iters; n += 2) {
-      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type());
+      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type(), std::false_type());
       __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads first
       consume(ta, tile_start(n), std::false_type());
-      fetch(ta, tile_start(n + 2), std::false_type(), std::true_type());
+      fetch(ta, tile_start(n + 2), std::false_type(), std::true_type(), std::false_type());
       __builtin_amdgcn_sched_barrier(0);
       consume(tb, tile_start(n + 1), std::false_type());
     }
     if (n + 1 < iters) {
-      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type());
+      fetch(tb, tile_start(n + 1), std::false_type(), std::true_type(), std::false_type());
       __builtin_amdgcn_sched_barrier(0);
       consume(ta, tile_start(n), std::false_type());
       consume(tb, tile_start(n + 1), std::false_type());
@@ -368,7 +389,7 @@ __device__ __forceinline__ void process_item(const DecodeParams &p, ItemShared<T
     // Ragged last tile.
     if (nfull * G::kTile < span && wave == nfull % W) {
       const int ts = tok0 + nfull * G::kTile;
-      fetch(ta, ts, std::true_type(), std::false_type());
+      fetch(ta, ts, std::true_type(), std::false_type(), std::false_type());
       consume(ta, ts, std::true_type());
     }
   }
@@ -536,8 +557,47 @@ constexpr int writer_seqs() {
 template <typename T, int D, int B, int W>
 __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, D, W> &sh, int h,
                                            int b, int part) {
-  int ctx = p.context_lens[b];
+  // Everything the first K/V loads need but the context length follows
+  // from (b, part): the two entries that pick the load policy and this
+  // wave's first-tile entries are loaded beside the context length, all as
+  // scalar loads (the kernel never writes these arrays) issued before the
+  // first wait, so the first K/V loads wait for one round trip instead of
+  // three.  The loads are unconditional, at indices clamped into the table
+  // rows; an entry read at a clamped index is never used: a tile that
+  // exists lies inside the row, and the next row's entry only counts when
+  // there is a next row.
+  const ConstI32 *row_s = (const ConstI32 *)(p.block_tables + (size_t)b * p.max_blocks_per_seq);
+  const int last_lb = p.max_blocks_per_seq - 1;
+  const int lb0 = min(part * p.partition_size / B, last_lb);
+  const bool has_next = b + 1 < p.num_seqs;
+  const int32_t e_here = row_s[lb0];
+  const int32_t e_next = row_s[(has_next ? p.max_blocks_per_seq : 0) + lb0];
+  FirstEntries<B> first;
+  {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lb = (part * p.partition_size + wave * 16) / B;
+#pragma unroll
+    for (int i = 0; i < FirstEntries<B>::kCount; ++i) first.e[i] = row_s[min(lb + i, last_lb)];
+  }
+  // The query row's chunks are loaded here too: they need only (b, h).
+  Chunk qc[Geometry<T, D>::kChunksPerLane];
+  load_q<T, D>(p, b, h, qc);
+  int ctx = ((const ConstI32 *)p.context_lens)[b];
+  // Keeps the entry loads above the branches below (the compiler would
+  // otherwise sink them past the context checks, one round trip later).
+  asm volatile("" ::"s"(e_here), "s"(e_next));
+#pragma unroll
+  for (int i = 0; i < FirstEntries<B>::kCount; ++i) asm volatile("" ::"s"(first.e[i]));
   ctx = ctx < 0 ? 0 : (ctx > p.max_context_len ? p.max_context_len : ctx);
+  // A partition whose first block the next sequence of the batch maps at the
+  // same logical index is read again by that sequence's workgroups: parallel
+  // samples share their prompt's blocks and sit next to each other in the
+  // batch, and with the head as the grid's fastest index their workgroups for
+  // one head run on the same XCD.  Such an item loads its K/V with the
+  // default, cache-retaining policy; every other item streams them
+  // non-temporally.  The next row's entry is only compared, never used as an
+  // address.
+  const bool keep = has_next && e_next == e_here;
   // With a fused append the item that owns the last token (partition 0 for
   // an empty context) reads it from the new rows; no item of the launch
   // reads that slot.
@@ -551,23 +611,10 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
     return;
   }
   if (part * p.partition_size >= ctx) return;
-  // A partition whose first block the next sequence of the batch maps at the
-  // same logical index is read again by that sequence's workgroups: parallel
-  // samples share their prompt's blocks and sit next to each other in the
-  // batch, and with the head as the grid's fastest index their workgroups for
-  // one head run on the same XCD.  Such an item loads its K/V with the
-  // default, cache-retaining policy; every other item streams them
-  // non-temporally.  The next row's entry is only compared, never used as an
-  // address (the index is below max_blocks_per_seq).  The two entries are
-  // read after the early returns: issued beside the context length they
-  // cost three VGPRs, which at B = 8 would lose the fifth wave per SIMD.
-  const int lb0 = part * p.partition_size / B;
-  const ConstI32 *row_s =
-      (const ConstI32 *)(p.block_tables + (size_t)b * p.max_blocks_per_seq);
-  if (b + 1 < p.num_seqs && row_s[p.max_blocks_per_seq + lb0] == row_s[lb0])
-    process_item<T, D, B, W, true>(p, sh, b, h, part, ctx, append);
+  if (keep)
+    process_item<T, D, B, W, true>(p, sh, b, h, part, ctx, append, first, qc);
   else
-    process_item<T, D, B, W, false>(p, sh, b, h, part, ctx, append);
+    process_item<T, D, B, W, false>(p, sh, b, h, part, ctx, append, first, qc);
 }
 
 // One workgroup per (head, sequence, partition); the hardware dispatcher
