@@ -625,8 +625,18 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
 // the launch is the smallest.  With a fused append the grid has one more
 // head column: its workgroups in the last-dispatched slice are the writers
 // (write_seq_rows), one per sequence; the others leave at once.
+// Waves per SIMD the decode kernels are compiled for: fp16 tiles fit 5 at
+// B < 16 (at most 96 VGPRs) and 4 otherwise (128); fp32 is left to the
+// compiler.
+template <typename T, int B>
+constexpr int decode_waves_per_eu() {
+  return sizeof(T) == 2 ? (B < 16 ? 5 : 4) : 1;
+}
+
 template <typename T, int D, int B, int W>
-__global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(64 * W)
+    __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, B>())))
+    decode_kernel(const DecodeParams p) {
   __shared__ ItemShared<T, D, W> sh;
   if ((int)blockIdx.x == p.num_heads) {
     if (blockIdx.z == gridDim.z - 1) write_seq_rows<T, D, B, W>(p, blockIdx.y);
@@ -640,7 +650,9 @@ __global__ void __launch_bounds__(64 * W) decode_kernel(const DecodeParams p) {
 // the smallest items trail the launch.  With a fused append, the rows past
 // the list are writers (write_new_rows), which fill the launch's tail.
 template <typename T, int D, int B, int W>
-__global__ void __launch_bounds__(64 * W) decode_listed_kernel(const DecodeParams p,
+__global__ void __launch_bounds__(64 * W)
+    __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, B>())))
+    decode_listed_kernel(const DecodeParams p,
                                                                 const WorkList items) {
   __shared__ ItemShared<T, D, W> sh;
   const int y = blockIdx.y;
