@@ -113,6 +113,44 @@ def test_prefill_edges(pa, oracle_lib, device):
     check(run_gpu(pa, wl, device), ref, "edges")
 
 
+def with_score_patterns(wl, patterns):
+    """wl with q = 1 everywhere and every K row of head h at position t set to
+    patterns[h](t) in each element, so that every query's score against key
+    t is D * patterns[h](t): a pattern the lazy reference of the online
+    softmax has to follow (slots past each context keep their NaN)."""
+    q = np.ones_like(wl.q)
+    kp = wl.k_pool.copy()
+    B = wl.block_size
+    for b, n in enumerate(wl.context_lens):
+        t = np.arange(int(n))
+        blk, off = wl.block_tables[b, t // B], t % B
+        for h, f in enumerate(patterns):
+            kp[blk, h, off, :] = f(t).astype(np.float32)[:, None]
+    return q, kp
+
+
+def test_prefill_lazy_reference_paths(pa, oracle_lib, device):
+    """Scores that move the softmax reference on every 32-key tile (rising by
+    about 21 log2 units per tile), never after the first (falling), and in
+    jumps of about 200 log2 units at sparse spikes: the rescale branch runs
+    often, with factors that underflow to 0, and the weights of keys far
+    below the reference underflow; grid and listed launches against the
+    oracle in fp64."""
+    announce("prefill lazy reference paths")
+    wl = W.prefill_small(seed=21, head_dim=128, num_heads=3, block_size=16,
+                         groups=((0, [600]), (300, [1, 90]), (0, [33])))
+    patterns = [lambda t: 0.04 * t,
+                lambda t: -0.04 * t,
+                lambda t: np.where(t % 97 == 0, 6.0, -6.0)]
+    q, kp = with_score_patterns(wl, patterns)
+    ref = oracle_lib.prefill(q, kp, wl.v_pool, wl.block_tables, wl.context_lens,
+                             wl.query_start, wl.scale)
+    assert np.isfinite(ref).all()
+    for listed in (False, True):
+        got = run_gpu(pa, wl, device, q=q, k_pool=kp, listed=listed)
+        check(got, ref, f"lazy reference, listed={listed}")
+
+
 def test_prefill_poisons_rows_that_see_a_bad_block(pa, oracle_lib, device):
     """A table entry outside the pool: rows whose context reaches that
     block are NaN, every other row is still right."""
