@@ -18,8 +18,12 @@
 //     whole loop).  The contraction over head_dim runs in a permuted order
 //     both operands share (lane group g takes the half [g*D/2, (g+1)*D/2)).
 //   * In the accumulator layout every lane holds 16 scores of one query
-//     per key block: the online softmax exchanges lanes l and l ^ 32 twice
-//     per tile, and rescaling the output is a per-lane multiply.
+//     per key block, and lanes l and l ^ 32 hold the same query.  The online
+//     softmax keeps a lazy reference per query: a tile's common path takes
+//     the weights against it with no maximum and no lane exchange, and only
+//     a weight sum that shows a weight of 2^11 or more sends the tile down a
+//     path that moves the reference (a max over the two lanes) and rescales
+//     the output, a per-lane multiply.
 //   * O^T += V^T P^T: P^T is the B operand straight from the score
 //     registers (converted to fp16, no shuffle); V^T, the A operand, comes
 //     from the row-major V tile by transposing LDS reads
@@ -334,18 +338,17 @@ struct SoftmaxState {
   float m = -INFINITY, m_use = 0.f, thr = -INFINITY, l = 0.f;
 };
 
-// The wave's products on one staged tile (keys t0 .. t0 + 31): scores, the
-// online softmax update and the output accumulation.
+// S^T = K Q^T for one staged tile (keys t0 .. t0 + 31), masked: slot i of
+// key block kb holds key t0 + 32 kb + 8 (i / 4) + 4 g + i % 4, set to -inf
+// when that key lies past the lane's query position, i.e. when its constant
+// part 32 kb + 8 (i / 4) + i % 4 exceeds pos - t0 - 4 g.  Tiles wholly at or
+// below every query of the wave skip the mask.
 template <int D>
-__device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_char *ks,
-                                              const Offsets<D> &o, const half8 (&qb)[D / 16],
-                                              float16v (&acc_o)[D / 32], SoftmaxState &sm,
-                                              int t0, const WaveRows &v, int g) {
+__device__ __forceinline__ void tile_scores(const lds_char *ks, const Offsets<D> &o,
+                                            const half8 (&qb)[D / 16], float16v (&s)[kKeyBlocks],
+                                            int t0, const WaveRows &v, int g) {
   using G = Geo<D>;
   constexpr int kSteps = D / 16;
-  const lds_char *vs = ks + G::kTensorBytes;
-  // S^T = K Q^T per 32-key block.
-  float16v s[kKeyBlocks];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb) {
     s[kb] = float16v{};
@@ -369,13 +372,6 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
-  // Online softmax for this lane's query over the tile's visible keys.
-  // The maximum is taken on raw scores (the scale is positive) and the
-  // scale is folded into the exponent: p = 2^(s * scale_log2 - m).
-  // Tiles wholly at or below every query of the wave skip the mask.
-  // Slot i of key block kb holds key t0 + 32 kb + 8 (i / 4) + 4 g + i % 4;
-  // it is masked when that key lies past the lane's query position, i.e.
-  // when its constant part 32 kb + 8 (i / 4) + i % 4 exceeds pos - t0 - 4 g.
   if (t0 + kKeys - 1 > v.wave_pos0) {
     const int lim = v.pos - t0 - 4 * g;
 #pragma unroll
@@ -384,20 +380,23 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
       for (int i = 0; i < 16; ++i)
         if (32 * kb + (i / 4) * 8 + (i % 4) > lim) s[kb][i] = -INFINITY;
   }
+}
+
+// The lazy step of the online softmax: a query whose tile maximum exceeds
+// its reference by more than kSlack (log2 units) takes that maximum as its
+// new reference, and its output and denominator are rescaled.  The maximum
+// is taken on raw scores (the scale is positive) against the threshold kept
+// in raw units; lanes l and l ^ 32 hold the same query and combine their
+// maxima, so both take the same step.
+template <int D>
+__device__ __forceinline__ void rebase(const PrefillParams &p, const float16v (&s)[kKeyBlocks],
+                                       float16v (&acc_o)[D / 32], SoftmaxState &sm) {
   float tile_max = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) tile_max = fmaxf(tile_max, s[kb][i]);
   tile_max = half_max(tile_max);
-  // Lazy rescaling: the reference moves only when this tile's max exceeds
-  // it by more than kSlack (log2 units); otherwise the weights of the tile
-  // are at most 2^kSlack, well inside fp16 and fp32.  Numerator and
-  // denominator share the reference, so the result is the same softmax.
-  // The test runs on the raw maximum (the scale is positive) against the
-  // threshold kept in raw units; the new reference, the rescaling of the
-  // output and of the denominator happen only when some query's reference
-  // moves.
   const bool bump = tile_max > sm.thr;
   if (__ballot(bump)) {
     const float m_new = tile_max * p.scale_log2;
@@ -411,21 +410,29 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
       sm.thr = (m_new + kSlack) / p.scale_log2;
     }
   }
-  const float m_use = sm.m_use;
-  // Weights rounded to fp16 (round to nearest even) two at a time.
-  unsigned pw[kKeyBlocks][8];
+}
+
+// Weights 2^(s * scale_log2 - m_use) rounded to fp16 (round to nearest
+// even) two at a time, and their sum over this lane's 16 keys (v_dot2
+// against ones, fp32), which is what the denominator adds: numerator and
+// denominator use the same rounded weights.  The pair conversion is written
+// as plain C, which compiles to one v_cvt_pk_f16_f32: the compiler then
+// also puts in the wait state that gfx950 needs between a transcendental
+// result (v_exp_f32) and a VALU read of it.  Inline assembly would hide
+// that read from it, and a schedule that placed the conversion right after
+// its exponential would read the exponential's input.
+__device__ __forceinline__ float tile_weights(const PrefillParams &p,
+                                              const float16v (&s)[kKeyBlocks], float m_use,
+                                              unsigned (&pw)[kKeyBlocks][8]) {
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], p.scale_log2, -m_use));
       const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], p.scale_log2, -m_use));
-      asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(pw[kb][i]) : "v"(e0), "v"(e1));
+      const half2v h = {(_Float16)e0, (_Float16)e1};
+      pw[kb][i] = __builtin_bit_cast(unsigned, h);
     }
-  // The denominator sums the fp16 weights the second product uses.  Each
-  // lane sums its own 16 keys of the tile; lanes l and l ^ 32 hold the same
-  // query with the same reference and scale factor, so their sums are added
-  // once, after the loop.
   float psum = 0.f;
   const half2v one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
@@ -433,6 +440,52 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pw[kb][i]), one, psum, false);
+  return psum;
+}
+
+// A lane's weight sum at or above this means one of its 16 weights is at
+// least 2^11 (or rounded to inf in fp16): the reference has to move.
+constexpr float kOverflowSum = 32768.f;
+
+// The wave's products on one staged tile (keys t0 .. t0 + 31): scores, the
+// online softmax update and the output accumulation.  kFirst: the wave's
+// first tile of its key range.
+template <int D, bool kFirst>
+__device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_char *ks,
+                                              const Offsets<D> &o, const half8 (&qb)[D / 16],
+                                              float16v (&acc_o)[D / 32], SoftmaxState &sm,
+                                              int t0, const WaveRows &v, int g) {
+  using G = Geo<D>;
+  const lds_char *vs = ks + G::kTensorBytes;
+  float16v s[kKeyBlocks];
+  tile_scores<D>(ks, o, qb, s, t0, v, g);
+  // The reference moves lazily (rebase).  On the wave's first tile it is
+  // set from the tile's maximum: a query's visible keys are a prefix of the
+  // sequence, so a query that sees any key of the range sees one in its
+  // first tile, and the largest weight it has seen is never below 1 from
+  // then on.  On later tiles the test runs on the weights, not on a
+  // maximum: the common path takes the weights against the current
+  // reference, and only when some lane's weight sum shows a weight of 2^11
+  // or more (or one beyond fp16, 2^16) are the scores taken again (they are
+  // not kept: registers), the reference moved and the weights redone.
+  // Weights stay below 2^16, inside fp16 and fp32; numerator and
+  // denominator share the reference, so the result is the same softmax.  A
+  // NaN score gives a NaN sum, which stays on the common path and reaches
+  // the row, as it should.
+  if constexpr (kFirst) rebase<D>(p, s, acc_o, sm);
+  unsigned pw[kKeyBlocks][8];
+  float psum = tile_weights(p, s, sm.m_use, pw);
+  if (!kFirst && __ballot(psum >= kOverflowSum)) {
+    // The clobber makes the scores' LDS reads happen again here: reusing the
+    // first reads would keep their 32 registers live across the weights.
+    asm volatile("" ::: "memory");
+    tile_scores<D>(ks, o, qb, s, t0, v, g);
+    rebase<D>(p, s, acc_o, sm);
+    psum = tile_weights(p, s, sm.m_use, pw);
+  }
+  // Each lane sums its own 16 keys of the tile; lanes l and l ^ 32 hold the
+  // same query with the same reference and scale factors, so their sums are
+  // added once, after the loop.
   sm.l += psum;
   half8 pb[kKeyBlocks][2];
 #pragma unroll
@@ -534,21 +587,24 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   // One tile: stage the next one into the other buffer, run the products on
   // this one, then wait for this wave's loads and meet the others.  The two
   // buffers alternate by template argument, so every LDS offset is an
-  // immediate.
-  auto step = [&](auto stage, int t0) {
+  // immediate.  The first tile of the range is peeled off the loop: it sets
+  // each query's softmax reference (tile_products<D, true>).
+  auto step = [&](auto stage, auto first, int t0) {
     constexpr int kS = decltype(stage)::value;
     lds_char *cur = kS ? lds1 : lds0;
     if (t0 + kKeys < k_hi)
       stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o, ent);
     ent = tile_entries<D, B>(it.table, w, it.kv_end, t0 + 2 * kKeys);
-    if (v.active && t0 <= v.wave_last) tile_products<D>(p, cur, o, qb, acc_o, sm, t0, v, g);
+    if (v.active && t0 <= v.wave_last)
+      tile_products<D, decltype(first)::value>(p, cur, o, qb, acc_o, sm, t0, v, g);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
     __syncthreads();
   };
-  for (int t0 = k_lo; t0 < k_hi; t0 += 2 * kKeys) {
-    step(std::integral_constant<int, 0>{}, t0);
+  if (k_lo < k_hi) step(std::integral_constant<int, 0>{}, std::true_type{}, k_lo);
+  for (int t0 = k_lo + kKeys; t0 < k_hi; t0 += 2 * kKeys) {
+    step(std::integral_constant<int, 1>{}, std::false_type{}, t0);
     if (t0 + kKeys >= k_hi) break;
-    step(std::integral_constant<int, 1>{}, t0 + kKeys);
+    step(std::integral_constant<int, 0>{}, std::false_type{}, t0 + kKeys);
   }
   const float l_run = half_sum(sm.l);   // the two lanes' partial denominators
 
