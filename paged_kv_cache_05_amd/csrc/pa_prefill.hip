@@ -524,17 +524,28 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// The tile's output rows (rows in range only).  Lane holds O^T[d][query c]
-// for d = 32 dt + 8 (i/4) + 4 g + (i%4).
+// The tile's output rows (rows in range only).  Lane (c, g) holds O^T[d][c]
+// for d = 32 dt + 8 (i / 4) + 4 g + (i % 4): 8-byte pieces of 32 rows.  The
+// wave normalises them, writes them to its own 32 rows of the (now idle)
+// stage buffers, row-major with 16-byte chunk ch of row r at ch ^ (r mod
+// kChunks) (so the writes of a chunk index by 32 rows spread over the
+// banks, and the reads of whole rows hit each bank once), and reads them
+// back as whole rows: each global store then writes 64 / kChunks complete
+// rows (16 bytes per lane) instead of 8 bytes in each of 32 rows.
 template <int D>
-__device__ __forceinline__ void store_rows(const PrefillParams &p, const Item &it,
-                                           const WaveRows &v, int g,
-                                           const float16v (&acc_o)[D / 32], float l_run) {
-  const int r = query_row(it, v);
-  if (r >= it.m || it.q0 + r >= p.num_query_rows || it.q0 + r < 0) return;
+__device__ __forceinline__ void store_rows(const PrefillParams &p, const Item &it, int w,
+                                           const float16v (&acc_o)[D / 32], float l_run,
+                                           lds_char *lds0, lds_char *lds1) {
+  using G = Geo<D>;
+  constexpr int kC = G::kChunks;
+  static_assert(2 * kRows * G::kRowBytes == G::kStageBytes, "two waves' rows per stage buffer");
+  lds_char *wb = (w < 2 ? lds0 : lds1) + (w & 1) * kRows * G::kRowBytes;
+  // The lane index is taken afresh (mbcnt) rather than from the value the
+  // loop's offsets were built from: reusing those would keep one more
+  // register live across the whole tile loop.
+  const int lane_now = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int c = lane_now & 31, g = lane_now >> 5;
   const float inv = (it.bad || !(l_run > 0.f)) ? NAN : 1.f / l_run;
-  _Float16 *orow =
-      static_cast<_Float16 *>(p.out) + ((int64_t)(it.q0 + r) * p.num_heads + it.h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -542,8 +553,26 @@ __device__ __forceinline__ void store_rows(const PrefillParams &p, const Item &i
       half4 o4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(acc_o[dt][i4 * 4 + e] * inv);
-      *reinterpret_cast<half4 *>(orow + dt * 32 + i4 * 8 + g * 4) = o4;
+      const int pos = (4 * dt + i4) ^ (c % kC);
+      *reinterpret_cast<__attribute__((address_space(3))) half4 *>(wb + c * G::kRowBytes +
+                                                                   pos * 16 + 8 * g) = o4;
     }
+  // This wave reads back only what it wrote itself; the wait and the
+  // clobber keep the reads behind the writes.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int kRowsPerStore = 64 / kC;
+  const int sub = lane_now / kC, ch = lane_now % kC;
+  const int r0 = it.qt * kQTile + w * kRows;   // the wave's first query row
+#pragma unroll
+  for (int k = 0; k < kRows / kRowsPerStore; ++k) {
+    const int row = k * kRowsPerStore + sub;
+    const half8 x =
+        *reinterpret_cast<const lds_half8 *>(wb + row * G::kRowBytes + ((ch ^ (row % kC)) * 16));
+    const int r = r0 + row;
+    if (r < it.m && it.q0 + r < p.num_query_rows && it.q0 + r >= 0)
+      *reinterpret_cast<half8 *>(static_cast<_Float16 *>(p.out) +
+                                 ((int64_t)(it.q0 + r) * p.num_heads + it.h) * D + ch * 8) = x;
+  }
 }
 
 // With nchunks > 1 the workgroup covers key chunk `chunk` of the tile's
@@ -625,7 +654,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     if (g == 0) p.part_ml[prow] = make_float2(sm.m, l_run);
     return;
   }
-  store_rows<D>(p, it, v, g, acc_o, l_run);
+  store_rows<D>(p, it, w, acc_o, l_run, lds0, lds1);
 }
 
 // Waves per SIMD the register budget is set for (168 VGPRs).  Two stages of
