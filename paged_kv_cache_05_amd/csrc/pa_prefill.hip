@@ -123,10 +123,6 @@ __device__ inline float half_sum(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-__device__ inline half8 load_half8(const _Float16 *p) {
-  return *reinterpret_cast<const half8 *>(p);
-}
-
 // Per-lane byte offsets, fixed for the whole loop.  Only the first offset
 // of each family is kept; the others differ from it in bits the swizzle
 // owns alone, so one XOR with a constant gives them (no carries: the
@@ -317,16 +313,39 @@ __device__ __forceinline__ int query_row(const Item &it, const WaveRows &v) {
   return v.pos - (it.n - it.m);
 }
 
-// The query fragments of lane (c, g): head-dim half g of query r.
+// The query tile goes through LDS: a wave's 32 query rows sit in the K
+// tile's layout (chunk ch of row r at ch ^ swz_k(r)), so the wave reads its
+// MFMA fragments with the K operand's offsets.  Waves 0 and 1 use the query
+// buffer, waves 2 and 3 the second stage buffer, which holds nothing until
+// the first step stages into it.
 template <int D>
-__device__ __forceinline__ void load_q(const PrefillParams &p, const Item &it, const WaveRows &v,
-                                       int g, half8 (&qb)[D / 16]) {
-  const int r = query_row(it, v);
-  const bool q_ok = r < it.m && !it.bad;
-  const _Float16 *row = static_cast<const _Float16 *>(p.q) +
-                        ((int64_t)(it.q0 + r) * p.num_heads + it.h) * D + g * (D / 2);
+__device__ __forceinline__ lds_char *q_block(int w, lds_char *ldsq, lds_char *lds1) {
+  return (w < 2 ? ldsq : lds1) + (w & 1) * kRows * Geo<D>::kRowBytes;
+}
+
+// Loads the wave's query rows straight into its block: each load covers
+// kLoadRows whole rows (16 bytes per lane), where lane-per-row reads of the
+// fragments would touch 64 rows per load.  Rows outside the chunk (a ragged
+// tile, or an item with inconsistent lengths) read query row 0 instead:
+// their columns of the products are independent of the others and their
+// output rows are never stored.  (B is not used: with D alone as its
+// parameter, the host pass of this compiler rejects the direct-to-LDS
+// builtin once callers of several block sizes share the function.)
+template <int D, int B>
+__device__ __forceinline__ void stage_queries(const PrefillParams &p, const Item &it, int w, int lane,
+                                        lds_char *qblk) {
+  using G = Geo<D>;
+  const int pos = lane % G::kChunks, sub = lane / G::kChunks;
+  const int r0 = it.qt * kQTile + w * kRows;   // the wave's first query of the chunk
+  const char *q = static_cast<const char *>(p.q);
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j) qb[j] = q_ok ? load_half8(row + 8 * j) : half8{};
+  for (int i = 0; i < kRows / G::kLoadRows; ++i) {
+    const int rr = i * G::kLoadRows + sub;     // row of the block this lane fills
+    const bool ok = r0 + rr < it.m && !it.bad;
+    const int64_t row = ok ? (int64_t)it.q0 + r0 + rr : 0;
+    const char *src = q + ((row * p.num_heads + it.h) * D) * 2 + ((pos ^ swz_k<D>(rr)) * 16);
+    __builtin_amdgcn_global_load_lds(src, qblk + i * G::kLoadRows * G::kRowBytes, 16, 0, 0);
+  }
 }
 
 // A lane's online-softmax state for its query.  m is the reference the
@@ -580,7 +599,8 @@ __device__ __forceinline__ void store_rows(const PrefillParams &p, const Item &i
 // result to slot `slot` for the merge pass.
 template <int D, int B>
 __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds0,
-                             lds_char *lds1, int chunk = 0, int nchunks = 1, int slot = 0) {
+                             lds_char *lds1, lds_char *ldsq, int chunk = 0, int nchunks = 1,
+                             int slot = 0) {
   const Item it = make_item(p, h, b, qt);
   if (it.empty) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -593,8 +613,8 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   const WaveRows v = wave_rows(it, w, c);
   const Offsets<D> o = make_offsets<D>(w, lane);
 
-  half8 qb[D / 16];
-  load_q<D>(p, it, v, g, qb);
+  lds_char *qblk = q_block<D>(w, ldsq, lds1);
+  stage_queries<D, B>(p, it, w, lane, qblk);
   float16v acc_o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc_o[t] = float16v{};
@@ -610,7 +630,13 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   // The next tile's entries are loaded one step ahead, so that their wait
   // falls under the product's LDS waits instead of before the staging.
   TileEntries<D, B> ent = tile_entries<D, B>(it.table, w, it.kv_end, k_lo + kKeys);
-  __builtin_amdgcn_s_waitcnt(0);   // query fragments and the first tile
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's query rows and first tile are in LDS
+  // The wave reads only the query rows it loaded itself, so its own wait
+  // covers them; the barrier then also keeps every wave's first staging into
+  // the second buffer behind waves 2 and 3 reading their rows there.
+  half8 qb[D / 16];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) qb[j] = *reinterpret_cast<const lds_half8 *>(qblk + off_rk(o, j));
   __syncthreads();
 
   // One tile: stage the next one into the other buffer, run the products on
@@ -671,8 +697,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(w
 prefill_kernel(const PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char ldsq[Geo<D>::kStageBytes];
   prefill_item<D, B>(p, blockIdx.x, blockIdx.z, (int)gridDim.y - 1 - (int)blockIdx.y,
-                     (lds_char *)lds0, (lds_char *)lds1);
+                     (lds_char *)lds0, (lds_char *)lds1, (lds_char *)ldsq);
 }
 
 // grid (heads, items): items = sequence << 16 | query tile, in the order the
@@ -682,9 +709,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(w
 prefill_listed_kernel(const PrefillParams p, const WorkList items) {
   __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char ldsq[Geo<D>::kStageBytes];
   const uint32_t it = items.item[blockIdx.y];
   prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds0,
-                     (lds_char *)lds1);
+                     (lds_char *)lds1, (lds_char *)ldsq);
 }
 
 // grid (heads, split list entries): one key chunk of one query tile each.
@@ -693,10 +721,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(w
 prefill_split_kernel(const PrefillParams p, const SplitList items) {
   __shared__ __attribute__((aligned(1024))) char lds0[Geo<D>::kStageBytes];
   __shared__ __attribute__((aligned(1024))) char lds1[Geo<D>::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char ldsq[Geo<D>::kStageBytes];
   const uint32_t it = items.item[blockIdx.y], part = items.part[blockIdx.y];
   prefill_item<D, B>(p, blockIdx.x, (int)(it >> 16), (int)(it & 0xffffu), (lds_char *)lds0,
-                     (lds_char *)lds1, (int)((part >> 4) & 15u), (int)(part & 15u) + 1,
-                     (int)(part >> 8));
+                     (lds_char *)lds1, (lds_char *)ldsq, (int)((part >> 4) & 15u),
+                     (int)(part & 15u) + 1, (int)(part >> 8));
 }
 
 // Merge of a split tile's chunks: grid (heads, split tiles, row groups),
