@@ -328,6 +328,8 @@ static int decode_impl(const char *what, void *out, const void *q, const void *n
     if (!new_key || !new_value || !slot_mapping) return PA_ERR_NULL;
     if (!aligned16(new_key) || !aligned16(new_value) || ((uintptr_t)slot_mapping & 7u))
       return PA_ERR_SHAPE;
+    // the grid launch adds ceil(num_seqs / num_heads) writer rows
+    if (num_seqs + (num_seqs + num_heads - 1) / num_heads > kGridYZ) return PA_ERR_SHAPE;
   }
   if (static_scratch) {
     workspace = scratch_on_current_device();

@@ -622,9 +622,12 @@ __device__ __forceinline__ void decode_one(const DecodeParams &p, ItemShared<T, 
 // the slowest grid dimension, counted down: the last partitions, which
 // exist only for the longest sequences, are dispatched first and partition
 // 0 (every row, including the short ones) last, so the work that trails
-// the launch is the smallest.  With a fused append the grid has one more
-// head column: its workgroups in the last-dispatched slice are the writers
-// (write_seq_rows), one per sequence; the others leave at once.
+// the launch is the smallest.  With a fused append the grid has
+// ceil(num_seqs / num_heads) more rows after the sequences: in the
+// last-dispatched slice, workgroup (x, num_seqs + r) stores the new rows of
+// sequence r * num_heads + x (write_seq_rows), so the writers are the last
+// workgroups of the launch and their scattered stores do not interleave
+// with the decode's reads; in the other slices those rows leave at once.
 // Waves per SIMD the decode kernels are compiled for: fp16 tiles fit 5 at
 // B < 16 (at most 96 VGPRs) and 4 otherwise (128); fp32 is left to the
 // compiler.
@@ -638,8 +641,11 @@ __global__ void __launch_bounds__(64 * W)
     __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<T, B>())))
     decode_kernel(const DecodeParams p) {
   __shared__ ItemShared<T, D, W> sh;
-  if ((int)blockIdx.x == p.num_heads) {
-    if (blockIdx.z == gridDim.z - 1) write_seq_rows<T, D, B, W>(p, blockIdx.y);
+  if ((int)blockIdx.y >= p.num_seqs) {
+    if (blockIdx.z == gridDim.z - 1) {
+      const int b = ((int)blockIdx.y - p.num_seqs) * p.num_heads + (int)blockIdx.x;
+      if (b < p.num_seqs) write_seq_rows<T, D, B, W>(p, b);
+    }
     return;
   }
   decode_one<T, D, B, W>(p, sh, blockIdx.x, blockIdx.y, p.num_partitions - 1 - (int)blockIdx.z);
@@ -738,7 +744,8 @@ hipError_t launch_typed(const DecodeParams &p, int num_seqs, Lists l, hipStream_
           <<<dim3(p.num_heads, l.merge_rows->count), D, 0, stream>>>(p, *l.merge_rows);
     return hipGetLastError();
   }
-  const dim3 grid(p.num_heads + (p.new_key != nullptr ? 1 : 0), num_seqs, p.num_partitions);
+  const int writer_rows = p.new_key != nullptr ? (num_seqs + p.num_heads - 1) / p.num_heads : 0;
+  const dim3 grid(p.num_heads, num_seqs + writer_rows, p.num_partitions);
   if (l.waves == 4) decode_kernel<T, D, B, 4><<<grid, 64 * 4, 0, stream>>>(p);
   else decode_kernel<T, D, B, W><<<grid, 64 * W, 0, stream>>>(p);
   if (p.num_partitions > 1)

@@ -166,6 +166,27 @@ def test_decode_rejects(pa, over, code):
     assert decode_call(pa.library(), **over) == code
 
 
+def append_call(lib, **over):
+    args = dict(out=OUT, q=Q, new_key=Q, new_value=Q, k_pool=KP, v_pool=VP, block_tables=TB,
+                context_lens=CL, slot_mapping=WS, num_seqs=4, num_heads=2, head_dim=64,
+                block_size=16, num_blocks=32, max_blocks_per_seq=4, max_context_len=50,
+                scale=0.125, dtype=1, partition_size=0, host_context_lens=None, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(over)
+    return lib.pa_decode_append(*args.values())
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation runs only without a GPU")
+@pytest.mark.parametrize("over,code", [
+    (dict(new_key=None), -1), (dict(slot_mapping=None), -1), (dict(new_value=Q + 8), -2),
+    (dict(slot_mapping=WS + 4), -2),
+    # the grid form adds ceil(num_seqs / num_heads) writer rows to the 65535-row grid
+    (dict(num_seqs=44000), -2), (dict(num_seqs=65000, num_heads=64), -2),
+])
+def test_decode_append_rejects(pa, over, code):
+    assert append_call(pa.library(), **over) == code
+
+
 def noalloc_call(lib, **over):
     args = dict(out=OUT, q=Q, k_pool=KP, v_pool=VP, block_tables=TB, context_lens=CL,
                 num_seqs=4, num_heads=2, head_dim=64, block_size=16, num_blocks=32,
