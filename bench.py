@@ -45,6 +45,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: HBM GB/s (% of peak), decode steps/s at OPT-13B shape"
 PEAK_HBM_GBS = 8000.0
+# decoder layers of the model whose layer shape each decode workload takes (OPT-13B, OPT-175B)
+MODEL_LAYERS = {"opt13b": 40, "short": 40, "long": 96}
 COUNTER_FILE = os.path.join(ROOT, "profiles", "pa_decode_opt13b_hbm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_05_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_kernels.h")]
@@ -839,6 +841,12 @@ def bench_decode(args):
         },
         "value_bytes": "sum ctx x H x D x 2 x 2 B + 4 B per block in use",
         "decode_steps_per_s": round(1000.0 / ms_per_step, 1),
+        "tokens_per_s": round(N * 1000.0 / ms_per_step, 1),
+        "model_equivalent_steps_per_s": {
+            "value": round(1000.0 / ms_per_step / MODEL_LAYERS[args.config], 1),
+            "layers": MODEL_LAYERS[args.config],
+            "what": "context only: this one layer's step rate divided by the model's layer count "
+                    "(attention alone, every layer the same shape)"},
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_bytes_per_call": decode_bytes,
         "new_rows_bytes_per_step": new_rows_bytes,
