@@ -287,8 +287,11 @@ int pa_decode_append(void *out, const void *q, const void *new_key, const void *
  * max_context_len) are host-side bounds that size the grid.
  * Only PA_F16 (PA_ERR_UNSUPPORTED otherwise); head_dim 64 or 128; block_size
  * 8, 16, 32 or 64.  The products run on MFMA with fp32 accumulation and an
- * fp32 softmax; the attention weights are rounded to fp16 for the product
- * with V.
+ * fp32 softmax.  Each query element is multiplied by scale * log2(e) in
+ * fp32 and rounded to fp16 once, before the products (a relative error of
+ * at most 2^-11 per element; |scale * q| must stay below 45000, or the
+ * rows turn inf/NaN); the attention weights are rounded to fp16 for the
+ * product with V.
  *
  * host_query_start (optional, host memory, num_seqs + 1 entries) is a host
  * copy of query_start: with it the library launches only the query tiles

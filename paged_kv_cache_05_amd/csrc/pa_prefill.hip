@@ -348,11 +348,12 @@ __device__ __forceinline__ void stage_queries(const PrefillParams &p, const Item
   }
 }
 
-// A lane's online-softmax state for its query.  m is the reference the
-// weights are taken against (log2 units, -inf until the query has seen a
-// key), m_use the same but 0 while m is -inf (so that weights of masked
-// keys come out 0, never NaN), thr the raw score above which the reference
-// moves, (m + kSlack) / scale_log2, and l this lane's partial denominator.
+// A lane's online-softmax state for its query.  Scores are in log2 units
+// (the query fragments carry scale * log2 e).  m is the reference the
+// weights are taken against (-inf until the query has seen a key), m_use the
+// same but 0 while m is -inf (so that weights of masked keys come out 0,
+// never NaN), thr the score above which the reference moves, m + kSlack,
+// and l this lane's partial denominator.
 struct SoftmaxState {
   float m = -INFINITY, m_use = 0.f, thr = -INFINITY, l = 0.f;
 };
@@ -402,14 +403,18 @@ __device__ __forceinline__ void tile_scores(const lds_char *ks, const Offsets<D>
 }
 
 // The lazy step of the online softmax: a query whose tile maximum exceeds
-// its reference by more than kSlack (log2 units) takes that maximum as its
-// new reference, and its output and denominator are rescaled.  The maximum
-// is taken on raw scores (the scale is positive) against the threshold kept
-// in raw units; lanes l and l ^ 32 hold the same query and combine their
-// maxima, so both take the same step.
-template <int D>
-__device__ __forceinline__ void rebase(const PrefillParams &p, const float16v (&s)[kKeyBlocks],
-                                       float16v (&acc_o)[D / 32], SoftmaxState &sm) {
+// its reference by more than kSlack takes that maximum as its new
+// reference, and its output and denominator are rescaled.  Lanes l and
+// l ^ 32 hold the same query and combine their maxima, so both take the
+// same step.  kFirst (the wave's first tile of its key range, where every
+// query that sees a key of the range sees one): the reference is set, to 0
+// when the tile's maximum lies in [kRefLo, kRefHi] (then the largest weight
+// is between 2^-8 and 2^11, inside fp16 with full precision, and the common
+// path needs no subtraction), else to the maximum.
+constexpr float kRefLo = -8.f, kRefHi = 11.f;
+template <int D, bool kFirst>
+__device__ __forceinline__ void rebase(const float16v (&s)[kKeyBlocks], float16v (&acc_o)[D / 32],
+                                       SoftmaxState &sm) {
   float tile_max = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
@@ -418,7 +423,8 @@ __device__ __forceinline__ void rebase(const PrefillParams &p, const float16v (&
   tile_max = half_max(tile_max);
   const bool bump = tile_max > sm.thr;
   if (__ballot(bump)) {
-    const float m_new = tile_max * p.scale_log2;
+    float m_new = tile_max;
+    if constexpr (kFirst) m_new = (tile_max >= kRefLo && tile_max <= kRefHi) ? 0.f : tile_max;
     const float alpha = bump ? __builtin_amdgcn_exp2f(sm.m - m_new) : 1.f;
     sm.l *= alpha;
 #pragma unroll
@@ -426,13 +432,14 @@ __device__ __forceinline__ void rebase(const PrefillParams &p, const float16v (&
     if (bump) {
       sm.m = m_new;
       sm.m_use = m_new;
-      sm.thr = (m_new + kSlack) / p.scale_log2;
+      sm.thr = m_new + kSlack;
     }
   }
 }
 
-// Weights 2^(s * scale_log2 - m_use) rounded to fp16 (round to nearest
-// even) two at a time, and their sum over this lane's 16 keys (v_dot2
+// Weights 2^(s - m_use) rounded to fp16 (round to nearest even) two at a
+// time (kZeroRef: m_use is 0 for every lane, and the subtraction is left
+// out; the weights are the same), and their sum over this lane's 16 keys (v_dot2
 // against ones, fp32), which is what the denominator adds: numerator and
 // denominator use the same rounded weights.  The pair conversion is written
 // as plain C, which compiles to one v_cvt_pk_f16_f32: the compiler then
@@ -440,15 +447,16 @@ __device__ __forceinline__ void rebase(const PrefillParams &p, const float16v (&
 // result (v_exp_f32) and a VALU read of it.  Inline assembly would hide
 // that read from it, and a schedule that placed the conversion right after
 // its exponential would read the exponential's input.
-__device__ __forceinline__ float tile_weights(const PrefillParams &p,
-                                              const float16v (&s)[kKeyBlocks], float m_use,
+template <bool kZeroRef>
+__device__ __forceinline__ float tile_weights(const float16v (&s)[kKeyBlocks], float m_use,
                                               unsigned (&pw)[kKeyBlocks][8]) {
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], p.scale_log2, -m_use));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], p.scale_log2, -m_use));
+      const float e0 = __builtin_amdgcn_exp2f(kZeroRef ? s[kb][2 * i] : s[kb][2 * i] - m_use);
+      const float e1 =
+          __builtin_amdgcn_exp2f(kZeroRef ? s[kb][2 * i + 1] : s[kb][2 * i + 1] - m_use);
       const half2v h = {(_Float16)e0, (_Float16)e1};
       pw[kb][i] = __builtin_bit_cast(unsigned, h);
     }
@@ -491,16 +499,17 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   // denominator share the reference, so the result is the same softmax.  A
   // NaN score gives a NaN sum, which stays on the common path and reaches
   // the row, as it should.
-  if constexpr (kFirst) rebase<D>(p, s, acc_o, sm);
+  if constexpr (kFirst) rebase<D, true>(s, acc_o, sm);
   unsigned pw[kKeyBlocks][8];
-  float psum = tile_weights(p, s, sm.m_use, pw);
+  float psum = __ballot(sm.m_use != 0.f) ? tile_weights<false>(s, sm.m_use, pw)
+                                         : tile_weights<true>(s, 0.f, pw);
   if (!kFirst && __ballot(psum >= kOverflowSum)) {
     // The clobber makes the scores' LDS reads happen again here: reusing the
     // first reads would keep their 32 registers live across the weights.
     asm volatile("" ::: "memory");
     tile_scores<D>(ks, o, qb, s, t0, v, g);
-    rebase<D>(p, s, acc_o, sm);
-    psum = tile_weights(p, s, sm.m_use, pw);
+    rebase<D, false>(s, acc_o, sm);
+    psum = tile_weights<false>(s, sm.m_use, pw);
   }
   // Each lane sums its own 16 keys of the tile; lanes l and l ^ 32 hold the
   // same query with the same reference and scale factors, so their sums are
@@ -637,6 +646,12 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   half8 qb[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) qb[j] = *reinterpret_cast<const lds_half8 *>(qblk + off_rk(o, j));
+  // Scores in log2 units: each query element times scale * log2 e, in fp32,
+  // rounded to fp16 once (a relative error of at most 2^-11 per element).
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[j][e] = (_Float16)((float)qb[j][e] * p.scale_log2);
   __syncthreads();
 
   // One tile: stage the next one into the other buffer, run the products on
