@@ -15,7 +15,8 @@
 // v_mfma_f32_32x32x16_f16:
 //   * S^T = K Q^T, one 32-key block at a time: key rows are the A operand,
 //     the wave's 32 query rows the B operand (kept in registers for the
-//     whole loop).  The contraction over head_dim runs in a permuted order
+//     whole loop, multiplied once by scale * log2 e, so that scores come out
+//     in log2 units).  The contraction over head_dim runs in a permuted order
 //     both operands share (lane group g takes the half [g*D/2, (g+1)*D/2)).
 //   * In the accumulator layout every lane holds 16 scores of one query
 //     per key block, and lanes l and l ^ 32 hold the same query.  The online
@@ -487,10 +488,10 @@ __device__ __forceinline__ void tile_products(const PrefillParams &p, const lds_
   float16v s[kKeyBlocks];
   tile_scores<D>(ks, o, qb, s, t0, v, g);
   // The reference moves lazily (rebase).  On the wave's first tile it is
-  // set from the tile's maximum: a query's visible keys are a prefix of the
-  // sequence, so a query that sees any key of the range sees one in its
-  // first tile, and the largest weight it has seen is never below 1 from
-  // then on.  On later tiles the test runs on the weights, not on a
+  // set from the tile's maximum (to 0 when that maximum is in [-8, 11]): a
+  // query's visible keys are a prefix of the sequence, so a query that sees
+  // any key of the range sees one in its first tile, and the largest weight
+  // it has seen is never below 2^-8 from then on.  On later tiles the test runs on the weights, not on a
   // maximum: the common path takes the weights against the current
   // reference, and only when some lane's weight sum shows a weight of 2^11
   // or more (or one beyond fp16, 2^16) are the scores taken again (they are
