@@ -184,26 +184,27 @@ __device__ inline Offsets<D> make_offsets(int w, int lane) {
 }
 
 // The table entries of this wave's rows [w kWaveRows, (w+1) kWaveRows) of
-// the tile at t0, loaded when those rows all precede kv_end (so the entries
-// lie inside the table row).  Uniform: scalar loads.  Nothing here reads the
-// loaded values, so the wait for them falls at their use in stage_rows.
+// the tile at t0.  Uniform: scalar loads, always issued, with the index
+// clamped to the table row (max_blocks_per_seq >= 1), so that no load
+// depends on the sequence's lengths; stage_rows uses the entries only when
+// the rows all precede kv_end.  Nothing here reads the loaded values, so the
+// wait for them falls at their use in stage_rows.
 template <int D, int B>
 struct TileEntries {
   static constexpr int kEnt = B >= Geo<D>::kWaveRows ? 1 : Geo<D>::kWaveRows / B;
   int32_t phys[kEnt];
-  bool in_row;
 };
 
 template <int D, int B>
-__device__ inline TileEntries<D, B> tile_entries(const int32_t *table, int w, int kv_end,
+__device__ inline TileEntries<D, B> tile_entries(const int32_t *table, int max_blocks, int w,
                                                  int t0) {
   using G = Geo<D>;
   TileEntries<D, B> e;
   const int key0 = t0 + w * G::kWaveRows;
-  e.in_row = key0 + G::kWaveRows <= kv_end;
   const auto *ctab = (const __attribute__((address_space(4))) int32_t *)table;
 #pragma unroll
-  for (int i = 0; i < TileEntries<D, B>::kEnt; ++i) e.phys[i] = e.in_row ? ctab[key0 / B + i] : 0;
+  for (int i = 0; i < TileEntries<D, B>::kEnt; ++i)
+    e.phys[i] = ctab[min(key0 / B + i, max_blocks - 1)];
   return e;
 }
 
@@ -220,7 +221,7 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
   const char *vp = static_cast<const char *>(p.v_pool);
   const uint64_t block_bytes = (uint64_t)p.num_heads * B * D * 2;
   const uint64_t head_bytes = (uint64_t)h * B * D * 2;
-  bool fast = ent.in_row;
+  bool fast = t0 + r0 + G::kWaveRows <= kv_end;   // the entries lie in the table row
 #pragma unroll
   for (int i = 0; i < TileEntries<D, B>::kEnt; ++i)
     fast = fast && ent.phys[i] >= 0 && ent.phys[i] < p.num_blocks;
@@ -611,9 +612,18 @@ template <int D, int B>
 __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_char *lds0,
                              lds_char *lds1, lds_char *ldsq, int chunk = 0, int nchunks = 1,
                              int slot = 0) {
-  const Item it = make_item(p, h, b, qt);
-  if (it.empty) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The entries of keys 0..31 (the first tile of every range that starts at
+  // key 0) are loaded beside the sequence's lengths, not after them.
+  const TileEntries<D, B> ent0 =
+      tile_entries<D, B>(p.block_tables + (int64_t)b * p.max_blocks_per_seq,
+                         p.max_blocks_per_seq, w, 0);
+  const Item it = make_item(p, h, b, qt);
+  // An empty use keeps the entries' loads here, in flight with the lengths'
+  // loads and waited for with them, instead of sunk to their use.
+#pragma unroll
+  for (int i = 0; i < TileEntries<D, B>::kEnt; ++i) asm volatile("" ::"s"(ent0.phys[i]));
+  if (it.empty) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 31;                 // this lane's query column / key row
   const int g = lane >> 5;                 // lane group
@@ -636,10 +646,11 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   const int k_hi = min(it.kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
   if (k_lo < k_hi)
     stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o,
-                     tile_entries<D, B>(it.table, w, it.kv_end, k_lo));
+                     k_lo == 0 ? ent0
+                               : tile_entries<D, B>(it.table, p.max_blocks_per_seq, w, k_lo));
   // The next tile's entries are loaded one step ahead, so that their wait
   // falls under the product's LDS waits instead of before the staging.
-  TileEntries<D, B> ent = tile_entries<D, B>(it.table, w, it.kv_end, k_lo + kKeys);
+  TileEntries<D, B> ent = tile_entries<D, B>(it.table, p.max_blocks_per_seq, w, k_lo + kKeys);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's query rows and first tile are in LDS
   // The wave reads only the query rows it loaded itself, so its own wait
   // covers them; the barrier then also keeps every wave's first staging into
@@ -665,7 +676,7 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
     lds_char *cur = kS ? lds1 : lds0;
     if (t0 + kKeys < k_hi)
       stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, t0 + kKeys, kS ? lds0 : lds1, o, ent);
-    ent = tile_entries<D, B>(it.table, w, it.kv_end, t0 + 2 * kKeys);
+    ent = tile_entries<D, B>(it.table, p.max_blocks_per_seq, w, t0 + 2 * kKeys);
     if (v.active && t0 <= v.wave_last)
       tile_products<D, decltype(first)::value>(p, cur, o, qb, acc_o, sm, t0, v, g);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have reached LDS
