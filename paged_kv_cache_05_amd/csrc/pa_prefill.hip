@@ -211,8 +211,10 @@ __device__ inline TileEntries<D, B> tile_entries(const int32_t *table, int max_b
 // Stages this wave's rows of the tile at t0 into the stage buffer st (K,
 // then V), given the rows' entries from tile_entries.  Rows whose entries
 // all lie in the pool take direct loads; the others the checked fetch.
+// True when the direct loads (2 kLoads of them) are still in flight on
+// return; the checked fetch has written its rows before it returns.
 template <int D, int B>
-__device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, int h, int w,
+__device__ inline bool stage_rows(const PrefillParams &p, const int32_t *table, int h, int w,
                                   int lane, int kv_end, int t0, lds_char *st,
                                   const Offsets<D> &o, const TileEntries<D, B> &ent) {
   using G = Geo<D>;
@@ -238,7 +240,7 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
       __builtin_amdgcn_global_load_lds(vp + base + o.gv,
                                        st + G::kTensorBytes + rj * G::kRowBytes, 16, 0, 0);
     }
-    return;
+    return true;
   }
   // Checked fetch: per lane, the same row and chunk as the direct load.
   const int pos = lane % G::kChunks, sub = lane / G::kChunks;
@@ -262,6 +264,7 @@ __device__ inline void stage_rows(const PrefillParams &p, const int32_t *table, 
     *reinterpret_cast<lds_half8 *>(st + rj * G::kRowBytes + lane * 16) = kx;
     *reinterpret_cast<lds_half8 *>(st + G::kTensorBytes + rj * G::kRowBytes + lane * 16) = vx;
   }
+  return false;
 }
 
 // One work item: head h, sequence b, query tile qt.
@@ -623,6 +626,8 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   // loads and waited for with them, instead of sunk to their use.
 #pragma unroll
   for (int i = 0; i < TileEntries<D, B>::kEnt; ++i) asm volatile("" ::"s"(ent0.phys[i]));
+  // The same for the pointers the staging needs (kernel arguments).
+  asm volatile("" ::"s"(p.q), "s"(p.k_pool), "s"(p.v_pool));
   if (it.empty) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 31;                 // this lane's query column / key row
@@ -644,17 +649,26 @@ __device__ void prefill_item(const PrefillParams &p, int h, int b, int qt, lds_c
   const int ntiles = (it.kv_end + kKeys - 1) / kKeys;
   const int k_lo = (int)((int64_t)ntiles * chunk / nchunks) * kKeys;
   const int k_hi = min(it.kv_end, (int)((int64_t)ntiles * (chunk + 1) / nchunks) * kKeys);
+  bool tile0_in_flight = false;
   if (k_lo < k_hi)
-    stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o,
+    tile0_in_flight = stage_rows<D, B>(p, it.table, h, w, lane, it.kv_end, k_lo, lds0, o,
                      k_lo == 0 ? ent0
                                : tile_entries<D, B>(it.table, p.max_blocks_per_seq, w, k_lo));
   // The next tile's entries are loaded one step ahead, so that their wait
   // falls under the product's LDS waits instead of before the staging.
   TileEntries<D, B> ent = tile_entries<D, B>(it.table, p.max_blocks_per_seq, w, k_lo + kKeys);
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's query rows and first tile are in LDS
+  // This wave's query rows are in LDS once no more than the first tile's
+  // direct loads are in flight (loads retire in order); the query scaling
+  // then runs under those.  vmcnt in bits 3:0; expcnt 6:4 and lgkmcnt 11:8
+  // at their maxima (no wait).
+  if (tile0_in_flight)
+    __builtin_amdgcn_s_waitcnt(0xf70 | (2 * Geo<D>::kLoads));
+  else
+    __builtin_amdgcn_s_waitcnt(0xf70);
   // The wave reads only the query rows it loaded itself, so its own wait
-  // covers them; the barrier then also keeps every wave's first staging into
-  // the second buffer behind waves 2 and 3 reading their rows there.
+  // covers them; the barrier (whose fences wait for the first tile) then
+  // also keeps every wave's first staging into the second buffer behind
+  // waves 2 and 3 reading their rows there.
   half8 qb[D / 16];
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) qb[j] = *reinterpret_cast<const lds_half8 *>(qblk + off_rk(o, j));
