@@ -134,14 +134,21 @@ def test_prefill_lazy_reference_paths(pa, oracle_lib, device):
     about 21 log2 units per tile), never after the first (falling), and in
     jumps of about 200 log2 units at sparse spikes: the rescale branch runs
     often, with factors that underflow to 0, and the weights of keys far
-    below the reference underflow; grid and listed launches against the
-    oracle in fp64."""
+    below the reference underflow.  Three more heads hold every score near
+    one level, about -49, +16 and -7.3 log2 units: the first tile's
+    reference is then its maximum (below -8 or above 11) or 0 (inside; the
+    largest weight is 2^-7.3).  A reference of 0 at -49 would round every
+    weight to 0 in fp16 and the rows to NaN.  Grid and listed launches
+    against the oracle in fp64."""
     announce("prefill lazy reference paths")
-    wl = W.prefill_small(seed=21, head_dim=128, num_heads=3, block_size=16,
+    wl = W.prefill_small(seed=21, head_dim=128, num_heads=6, block_size=16,
                          groups=((0, [600]), (300, [1, 90]), (0, [33])))
     patterns = [lambda t: 0.04 * t,
                 lambda t: -0.04 * t,
-                lambda t: np.where(t % 97 == 0, 6.0, -6.0)]
+                lambda t: np.where(t % 97 == 0, 6.0, -6.0),
+                lambda t: -3.0 + 0.05 * np.sin(t),
+                lambda t: 1.0 + 0.05 * np.sin(t),
+                lambda t: -0.45 + 0.02 * np.cos(t)]
     q, kp = with_score_patterns(wl, patterns)
     ref = oracle_lib.prefill(q, kp, wl.v_pool, wl.block_tables, wl.context_lens,
                              wl.query_start, wl.scale)
