@@ -387,9 +387,10 @@ __device__ __forceinline__ void tile_scores(const lds_char *ks, const Offsets<D>
   // Schedule: the K operand reads run kAhead steps ahead of the score
   // MFMAs (LDS reads, then one MFMA and one read per step), so that the
   // reads of later steps return under the earlier MFMAs instead of each
-  // pair waiting for its own.  Three steps ahead keeps every instantiation
-  // within the three-waves-per-SIMD register budget without scratch.
-  constexpr int kAhead = kSteps < 3 ? kSteps : 3;
+  // pair waiting for its own.  Four steps ahead at D = 128 (168 VGPRs, the
+  // whole three-waves-per-SIMD budget, no scratch) and three at D = 64,
+  // where four (every read at once) measured slower.
+  constexpr int kAhead = kSteps >= 8 ? 4 : (kSteps < 3 ? kSteps : 3);
   __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // LDS reads
 #pragma unroll
   for (int j = 0; j < kSteps - kAhead; ++j) {
